@@ -1,0 +1,322 @@
+"""Throughput of the n-gram memory hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic tokens:
+canonical map, n-grams, hashes, rows, gather/dequant/sign (pg_index_gather),
+then the W_V projection and fusion (pg_project_gate) -- the two kernels that
+pg_forward launches, called here one after the other so that HIP events can
+bracket each kernel on the stream they run on. Steps cycle through a pool of
+32 distinct token batches already resident in HBM, so the table rows of one
+step are not left in the caches by the previous one.
+
+Prints one JSON line: whole-job tokens/s, the roofline position of the
+dominant kernel (algorithmic bytes or flops per launch over its mean event
+duration), both kernels' figures, and the CPU oracle timed on a bounded
+sample on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+POOL = 32
+DEFAULT_WORKLOAD = "pagegram200m_bf16_8x2048"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=16384)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a 1 GiB device copy (for counter scaling)")
+    return p.parse_args()
+
+
+def algorithmic_costs(wl):
+    """Per-token algorithmic HBM bytes of index+gather and flops/bytes of the
+    projection stage (the figures the roofline uses)."""
+    lay = wl["layout"]
+    O = lay["n_max"] - lay["n_min"] + 1
+    K, r = lay["K"], lay["r"]
+    elt = 4 if wl["act_dtype"] == "f32" else 2
+    row_bytes = {"f32": 4 * r, "bf16": 2 * r, "nf4": r // 2 + 2}[wl["table_dtype"]]
+    E = O * K * r
+    gather_bytes = 4 + O * K * row_bytes + E * elt
+    if wl["gate"] == "engram":
+        M, d = wl["M"], wl["d"]
+        flops = 2 * E * (1 + M) * d
+        proj_bytes = E * elt + 2 * M * d * elt   # e in; h in, out (pass 1 + 2 read h)
+    else:
+        d = wl["d"]
+        flops = 2 * E * d
+        proj_bytes = E * elt + 2 * d * elt       # e in; x in, out
+    return dict(gather_bytes=gather_bytes, proj_flops=flops, proj_bytes=proj_bytes, E=E)
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gather": ["hashed_head_gram_amd/csrc/index.hip", "hashed_head_gram_amd/csrc/common.h"],
+    "projection": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
+}
+
+
+def traffic_for(stage, workload):
+    """HBM bytes per launch from committed counter runs, if the kernel source
+    is unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(stage)
+    if not ent or ent.get("source_digest") != source_digest(KERNEL_SOURCES[stage]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, n_tok):
+    """The CPU oracle on the first n_tok tokens of the workload's stream."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import configs
+
+    T = wl["T"]
+    B = max(1, min(wl["B"], n_tok // T)) if n_tok >= T else 1
+    Tn = T if n_tok >= T else n_tok
+    sub = configs.with_tokens(wl, B, Tn)
+    toks = synth.tokens(wl)[:B, :Tn]
+    cmap = synth.canon_map(wl)
+    pad = wl["canon_vocab"]
+    lay = wl["layout"]
+    # Materialise the touched rows and the dense inputs first (input
+    # generation, not timed).
+    idx = oracle.index(lay, toks, cmap, pad)
+    uniq = np.unique(idx["rows"].reshape(-1))
+    stored = synth.table_rows(wl, uniq)
+
+    def fetch(rows):
+        at = np.searchsorted(uniq, rows)
+        if isinstance(stored, tuple):
+            return stored[0][at], stored[1][at]
+        return stored[at]
+    W = synth.weight(wl)
+    if wl["act_dtype"] == "bf16":
+        W = synth.bf16_bits_to_f32(W)
+    N = B * Tn
+    t0 = time.perf_counter()
+    if wl["gate"] == "scalar":
+        x = synth.resid_rows(wl, np.arange(N))
+        if wl["act_dtype"] == "bf16":
+            x = synth.bf16_bits_to_f32(x)
+        t0 = time.perf_counter()
+        oracle.forward_scalar(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["g"],
+                              lambda p: x[p])
+    else:
+        gh, gk, gu, cw = synth.engram_params(wl)
+        M, Ntot = wl["M"], wl["B"] * wl["T"]
+        rows_h = np.concatenate([m * Ntot + (np.arange(B)[:, None] * T
+                                             + np.arange(Tn)[None, :]).reshape(-1)
+                                 for m in range(M)])
+        hh = synth.bf16_bits_to_f32(synth.resid_rows(wl, rows_h)).reshape(M, N, -1)
+        t0 = time.perf_counter()
+        oracle.forward_engram(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["d"],
+                              M, gh, gk, gu, cw, wl["conv_dil"], wl["eps"],
+                              lambda m, f: hh[m, f])
+    dt = time.perf_counter() - t0
+    del sub
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"value": N / dt / 1e6, "unit": "Mtok/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"first {B}x{Tn} tokens of the stream ({N} tokens), {dt:.2f} s; "
+                      f"index and gather single-threaded numpy, fp64 GEMM on "
+                      f"{blas} BLAS threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange between GPUs)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import hashed_head_gram_amd as pg
+    import synth
+    from synth import configs, device as sdev
+
+    dev = torch.device("cuda:0")
+    wl = configs.workload(args.workload)
+    lay_d = wl["layout"]
+    layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
+                            pages=lay_d["pages"], head_rows=lay_d["head_rows"],
+                            hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
+                            n_min=lay_d["n_min"], n_max=lay_d["n_max"],
+                            pad_id=wl["canon_vocab"])
+    R = pg.pg_layout_rows(layout)
+    r = lay_d["r"]
+    B, T = wl["B"], wl["T"]
+    N = B * T
+    costs = algorithmic_costs(wl)
+    E = costs["E"]
+    act = torch.float32 if wl["act_dtype"] == "f32" else torch.bfloat16
+    e_dtype = pg.PG_F32 if wl["act_dtype"] == "f32" else pg.PG_BF16
+
+    # Inputs, resident in HBM before timing.
+    if wl["table_dtype"] == "nf4":
+        codes = torch.empty(R, r // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(R, dtype=torch.float16, device=dev)
+        sdev.fill_nf4_table(codes, scales, wl["table_seed"])
+        table = pg.make_table(pg.PG_NF4, codes, R, scales=scales)
+    else:
+        tdt = torch.float32 if wl["table_dtype"] == "f32" else torch.bfloat16
+        tab = torch.empty(R, r, dtype=tdt, device=dev)
+        sdev.fill_normal(tab, wl["table_seed"], configs.STREAM_TABLE, wl["table_sigma"])
+        table = pg.make_table(pg.PG_F32 if wl["table_dtype"] == "f32" else pg.PG_BF16,
+                              tab, R)
+    cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
+    pool = [torch.from_numpy(synth.tokens(wl, batch=j)).to(dev) for j in range(POOL)]
+    d_out = configs.d_out(wl)
+    W = torch.empty(d_out, E, dtype=act, device=dev)
+    sdev.fill_normal(W, wl["data_seed"], configs.STREAM_W, wl["w_sigma"])
+    if wl["gate"] == "engram":
+        M = wl["M"]
+        gh, gk, gu, cw = (torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+                          for a in synth.engram_params(wl))
+        fuse = pg.make_fuse(pg.PG_GATE_ENGRAM, e_dtype, wl["d"], M=M, eps=wl["eps"],
+                            gamma_h=gh, gamma_k=gk, gamma_u=gu, conv_w=cw,
+                            conv_k=wl["conv_k"], conv_dil=wl["conv_dil"])
+        resid = torch.empty(M * N, wl["d"], dtype=act, device=dev)
+        out = torch.empty(M * N, wl["d"], dtype=act, device=dev)
+    else:
+        fuse = pg.make_fuse(pg.PG_GATE_SCALAR, e_dtype, wl["d"], g=wl["g"])
+        resid = torch.empty(N, wl["d"], dtype=act, device=dev)
+        out = torch.empty(N, wl["d"], dtype=act, device=dev)
+    sdev.fill_normal(resid, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
+    e = torch.empty(N, E, dtype=act, device=dev)
+    ws = torch.empty(max(pg.pg_workspace_size(None, fuse, B, T), 256), dtype=torch.uint8,
+                     device=dev)
+    ws_fwd = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8,
+                         device=dev)
+    torch.cuda.synchronize()
+
+    # pg_forward launches exactly these two kernels; check once that the
+    # two-call step reproduces it bit for bit.
+    out_fwd = torch.empty_like(out)
+    pg.pg_forward(layout, table, fuse, pool[0], cmap, W, resid, out_fwd, ws_fwd)
+    pg.pg_index_gather(layout, table, pool[0], cmap, e_dtype, e)
+    pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws)
+    torch.cuda.synchronize()
+    same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
+    del out_fwd, ws_fwd
+
+    def step(j, ev=None):
+        toks = pool[j % POOL]
+        if ev is not None:
+            ev[0].record()
+        pg.pg_index_gather(layout, table, toks, cmap, e_dtype, e)
+        if ev is not None:
+            ev[1].record()
+        pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws)
+        if ev is not None:
+            ev[2].record()
+
+    for j in range(args.warmup):
+        step(j)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(j, events[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g_ms = np.array([ev[0].elapsed_time(ev[1]) for ev in events])
+    p_ms = np.array([ev[1].elapsed_time(ev[2]) for ev in events])
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall / args.steps * 1e3
+    tok_s = N / (ms_per_step / 1e3)
+    g_bytes = costs["gather_bytes"] * N
+    p_flops = costs["proj_flops"] * N
+    p_bytes = costs["proj_bytes"] * N
+    g_gbps = g_bytes / (g_ms.mean() / 1e3) / 1e9
+    p_peak = FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS
+    p_tflops = p_flops / (p_ms.mean() / 1e3) / 1e12
+    gather = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
+              "ms_p10": float(np.percentile(g_ms, 10)), "ms_p90": float(np.percentile(g_ms, 90)),
+              "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
+              "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
+              "traffic": traffic_for("gather", wl["name"])}
+    proj = {"kernel": "gemm_bf16_kernel" if act == torch.bfloat16 else "gemm_f32_kernel",
+            "ms_mean": float(p_ms.mean()), "ms_p10": float(np.percentile(p_ms, 10)),
+            "ms_p90": float(np.percentile(p_ms, 90)), "flops_per_launch": p_flops,
+            "achieved_TFLOPs": p_tflops, "frac_mfma_peak": p_tflops / p_peak,
+            "bytes_per_launch": p_bytes,
+            "achieved_GBps": p_bytes / (p_ms.mean() / 1e3) / 1e9,
+            "traffic": traffic_for("projection", wl["name"])}
+    if g_ms.mean() >= p_ms.mean():
+        roof = {"kernel": gather["kernel"], "bound": "hbm", "achieved": g_gbps,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
+                "traffic": gather["traffic"]}
+    else:
+        roof = {"kernel": proj["kernel"], "bound": "mfma", "achieved": p_tflops,
+                "peak": p_peak, "unit": "TFLOP/s", "frac": p_tflops / p_peak,
+                "traffic": proj["traffic"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_tokens)
+    line = {
+        "metric": "M tokens/s for hash+gather+project; gather HBM GB/s and % of peak",
+        "value": tok_s / 1e6, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl["act_dtype"],
+        "data": "synthetic (seeded Zipf token streams, counter-generated table and weights)",
+        "config": {"workload": wl["name"], "tokens_per_step": N, "batch": B, "seq_len": T,
+                   "layout": lay_d["kind"], "K": lay_d["K"], "S": lay_d["S"], "r": r,
+                   "table_dtype": wl["table_dtype"], "table_rows": R, "d": wl["d"],
+                   "gate": wl["gate"], "token_pool": POOL},
+        "roofline": roof,
+        "gather": gather,
+        "projection": proj,
+        "forward_matches_two_calls": bool(same),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,302 @@
+// C ABI entry points: argument validation, layout preparation, dispatch.
+// Every check that can fail runs before anything is enqueued.
+#include <limits.h>
+
+#include "common.h"
+
+namespace pg {
+hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
+                               int64_t d, int64_t Mbr, const void* h,
+                               const float* gamma_h, const float* gamma_k, uint16_t* v,
+                               float* part_v, float* part_k, hipStream_t s);
+}
+
+namespace {
+
+using pg::DevLayout;
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+constexpr int64_t kRowLimit = (int64_t)1 << 62;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Validate a pg_layout and fill the kernels' view of it.
+int prepare_layout(const pg_layout* in, DevLayout* L) {
+  if (!in) return PG_EINVAL;
+  if (in->kind != PG_PAGEGRAM && in->kind != PG_ENGRAM) return PG_EINVAL;
+  if (in->n_min < 1 || in->n_max < in->n_min || in->n_max > PG_MAX_ORDERS) return PG_EINVAL;
+  if (in->K < 1 || in->K > PG_MAX_HEADS) return PG_EINVAL;
+  if (in->r < 1 || in->r > 64 * pg::kMaxSignWords) return PG_EINVAL;
+  if (in->pad_id < 0) return PG_EINVAL;
+  if (in->use_signs != 0 && in->use_signs != 1) return PG_EINVAL;
+  *L = DevLayout{};
+  L->kind = in->kind;
+  L->n_min = in->n_min;
+  L->O = in->n_max - in->n_min + 1;
+  L->K = in->K;
+  L->r = in->r;
+  L->W = (in->r + 63) / 64;
+  L->use_signs = in->use_signs;
+  L->n_roles = L->O * (1 + L->K + L->K * L->W);
+  L->seed = in->hash_seed;
+  L->pad_id = (uint64_t)(uint32_t)in->pad_id;
+  int64_t acc = 0;
+  if (in->kind == PG_PAGEGRAM) {
+    if (in->S < 1) return PG_EINVAL;
+    L->S = (uint64_t)in->S;
+    L->S_magic = UINT64_MAX / L->S;
+    const int64_t per_page = (int64_t)in->K * in->S;
+    for (int i = 0; i < L->O; ++i) {
+      const int64_t P = in->pages[i];
+      if (P < 1) return PG_EINVAL;
+      if (P > (kRowLimit - acc) / per_page) return PG_ERANGE;
+      L->P[i] = (uint64_t)P;
+      L->P_magic[i] = UINT64_MAX / (uint64_t)P;
+      L->base[i] = acc;
+      acc += P * per_page;
+    }
+  } else {
+    L->S = 1;
+    L->S_magic = UINT64_MAX;
+    for (int i = 0; i < L->O; ++i)
+      for (int k = 0; k < L->K; ++k) {
+        const int64_t P = in->head_rows[i][k];
+        if (P < 1) return PG_EINVAL;
+        if (P > kRowLimit - acc) return PG_ERANGE;
+        const int hk = i * pg::kMaxHeads + k;
+        L->Pk[hk] = (uint64_t)P;
+        L->Pk_magic[hk] = UINT64_MAX / (uint64_t)P;
+        L->base_k[hk] = acc;
+        acc += P;
+      }
+  }
+  L->n_rows = acc;
+  return PG_OK;
+}
+
+int table_e_dtype(int32_t table_dtype) { return table_dtype == PG_F32 ? PG_F32 : PG_BF16; }
+
+int check_table(const DevLayout& L, const pg_table* t) {
+  if (!t || !t->data) return PG_EINVAL;
+  if (!aligned(t->data, 16)) return PG_EINVAL;
+  if (t->n_rows != L.n_rows) return PG_EINVAL;
+  switch (t->dtype) {
+    case PG_F32:
+      if (L.r % 4) return PG_EUNSUPPORTED;
+      break;
+    case PG_BF16:
+      if (L.r % 8) return PG_EUNSUPPORTED;
+      break;
+    case PG_NF4:
+      if (L.r % 32) return PG_EUNSUPPORTED;
+      if (!t->scales || !aligned(t->scales, 2)) return PG_EINVAL;
+      break;
+    default:
+      return PG_EINVAL;
+  }
+  return PG_OK;
+}
+
+int check_tokens(const int32_t* tokens, int64_t B, int64_t T, const int32_t* cmap, int64_t V) {
+  if (B < 0 || T < 0) return PG_EINVAL;
+  if (T > 0 && B > kMaxTokens / T) return PG_ERANGE;
+  if (B * T == 0) return PG_OK;
+  if (!tokens || !cmap || V < 1) return PG_EINVAL;
+  return PG_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PG_OK : PG_EHIP; }
+
+int check_fuse(const pg_fuse* f, int64_t B, int64_t T, int64_t e_dim) {
+  if (!f) return PG_EINVAL;
+  if (f->gate != PG_GATE_SCALAR && f->gate != PG_GATE_ENGRAM) return PG_EINVAL;
+  if (f->dtype != PG_F32 && f->dtype != PG_BF16) return PG_EINVAL;
+  if (f->d < 1 || e_dim < 1) return PG_EINVAL;
+  if (B < 0 || T < 0) return PG_EINVAL;
+  if (T > 0 && B > kMaxTokens / T) return PG_ERANGE;
+  if (e_dim > INT_MAX) return PG_ERANGE;
+  if (f->increment_only != 0 && f->increment_only != 1) return PG_EINVAL;
+  if (f->dtype == PG_BF16 && e_dim % 8) return PG_EUNSUPPORTED;
+  if (f->dtype == PG_F32 && e_dim % 4) return PG_EUNSUPPORTED;
+  if (f->gate == PG_GATE_ENGRAM) {
+    if (f->dtype != PG_BF16) return PG_EUNSUPPORTED;
+    if (f->d % 128) return PG_EUNSUPPORTED;
+    if (f->M < 1 || f->M > 8) return PG_EINVAL;
+    if (f->conv_k < 1 || f->conv_k > 8 || f->conv_dil < 1) return PG_EINVAL;
+    if ((int64_t)(f->conv_k - 1) * f->conv_dil > 64) return PG_EUNSUPPORTED;
+    if (!f->gamma_h || !f->gamma_k || !f->gamma_u || !f->conv_w) return PG_EINVAL;
+    if (!(f->eps >= 0.0f)) return PG_EINVAL;
+    if (B > 65535) return PG_EUNSUPPORTED;
+    if ((int64_t)(1 + f->M) * f->d > INT_MAX) return PG_ERANGE;
+  }
+  return PG_OK;
+}
+
+int64_t project_workspace(const pg_fuse* f, int64_t N) {
+  if (f->gate == PG_GATE_ENGRAM) return pg::engram_workspace_bytes(N, f->d, f->M);
+  return 0;
+}
+
+int64_t elt_bytes(int32_t dt) { return dt == PG_F32 ? 4 : 2; }
+
+// Projection + fusion on an e already in device memory.
+int run_project(const pg_fuse* f, const void* e, int64_t B, int64_t T, int64_t e_dim,
+                const void* W, const void* resid, void* out, void* ws, hipStream_t s) {
+  const int64_t N = B * T;
+  if (f->gate == PG_GATE_SCALAR) {
+    const void* x = f->increment_only ? nullptr : resid;
+    return hip_status(pg::launch_project_scalar(f->dtype, e, N, e_dim, W, f->d, f->g, x, out, s));
+  }
+  return hip_status(pg::launch_engram(e, B, T, e_dim, W, f->d, f->M, f->eps, f->gamma_h,
+                                      f->gamma_k, f->gamma_u, f->conv_w, f->conv_k,
+                                      f->conv_dil, resid, out, ws, f->increment_only ? 0 : 1,
+                                      s));
+}
+
+}  // namespace
+
+extern "C" {
+
+PG_API const char* pg_strerror(int status) {
+  switch (status) {
+    case PG_OK: return "ok";
+    case PG_EINVAL: return "invalid argument (NULL pointer, size, alignment or layout)";
+    case PG_EUNSUPPORTED: return "unsupported shape or dtype combination";
+    case PG_EHIP: return "HIP launch or runtime error";
+    case PG_ERANGE: return "size out of range";
+    default: return "unknown status";
+  }
+}
+
+PG_API uint32_t pg_hash_version(void) { return 1u; }
+
+PG_API int pg_layout_rows(const pg_layout* layout, int64_t* n_rows) {
+  if (!n_rows) return PG_EINVAL;
+  DevLayout L;
+  const int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  *n_rows = L.n_rows;
+  return PG_OK;
+}
+
+PG_API int64_t pg_workspace_size(const pg_layout* layout, const pg_fuse* fuse, int64_t B,
+                                 int64_t T) {
+  if (!fuse || B < 0 || T < 0) return PG_EINVAL;
+  if (T > 0 && B > kMaxTokens / T) return PG_ERANGE;
+  const int64_t N = B * T;
+  int64_t bytes = 0;
+  if (layout) {
+    DevLayout L;
+    const int st = prepare_layout(layout, &L);
+    if (st != PG_OK) return st;
+    bytes += align256(N * (int64_t)L.O * L.K * L.r * elt_bytes(fuse->dtype));
+  }
+  if (fuse->gate == PG_GATE_ENGRAM) {
+    if (fuse->d < 1 || fuse->M < 1 || fuse->M > 8) return PG_EINVAL;
+  }
+  return bytes + project_workspace(fuse, N);
+}
+
+PG_API int pg_index(const pg_layout* layout, const int32_t* tokens, int64_t B, int64_t T,
+                    const int32_t* canon_map, int64_t V, int32_t* canon_out,
+                    uint64_t* hash_out, int64_t* rows_out, int64_t* pages_out,
+                    uint64_t* signs_out, int32_t* dev_status, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  if (B * T == 0) return PG_OK;
+  if (!rows_out || !signs_out) return PG_EINVAL;
+  return hip_status(pg::launch_index(L, tokens, B, T, canon_map, V, canon_out, hash_out,
+                                     rows_out, pages_out, signs_out, dev_status, stream));
+}
+
+PG_API int pg_gather(const pg_layout* layout, const pg_table* table, const int64_t* rows,
+                     const uint64_t* signs, int64_t n_tok, int32_t e_dtype, void* e_out,
+                     hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  if (n_tok < 0) return PG_EINVAL;
+  if (n_tok > kMaxTokens) return PG_ERANGE;
+  if (e_dtype != table_e_dtype(table->dtype)) return PG_EUNSUPPORTED;
+  if (n_tok == 0) return PG_OK;
+  if (!rows || !e_out || !aligned(e_out, 16)) return PG_EINVAL;
+  if (!signs && L.use_signs) return PG_EINVAL;
+  return hip_status(pg::launch_gather(L, table->dtype, table->data, table->scales, rows,
+                                      signs, n_tok, e_out, stream));
+}
+
+PG_API int pg_index_gather(const pg_layout* layout, const pg_table* table,
+                           const int32_t* tokens, int64_t B, int64_t T,
+                           const int32_t* canon_map, int64_t V, int32_t e_dtype,
+                           void* e_out, int32_t* dev_status, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  if (e_dtype != table_e_dtype(table->dtype)) return PG_EUNSUPPORTED;
+  if (B * T == 0) return PG_OK;
+  if (!e_out || !aligned(e_out, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales,
+                                            tokens, B, T, canon_map, V, e_out, dev_status,
+                                            stream));
+}
+
+PG_API int pg_project_gate(const pg_fuse* fuse, const void* e, int64_t B, int64_t T,
+                           int64_t e_dim, const void* W, const void* resid, void* out,
+                           void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  int st = check_fuse(fuse, B, T, e_dim);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!e || !W || !out) return PG_EINVAL;
+  if (!aligned(e, 16) || !aligned(W, 16) || !aligned(out, 16)) return PG_EINVAL;
+  if (resid && !aligned(resid, 16)) return PG_EINVAL;
+  if (fuse->gate == PG_GATE_ENGRAM && !resid) return PG_EINVAL;
+  const int64_t need = project_workspace(fuse, N);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PG_EINVAL;
+  return run_project(fuse, e, B, T, e_dim, W, resid, out, workspace, stream);
+}
+
+PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_fuse* fuse,
+                      const int32_t* tokens, int64_t B, int64_t T, const int32_t* canon_map,
+                      int64_t V, const void* W, const void* resid, void* out,
+                      void* workspace, int64_t workspace_bytes, int32_t* dev_status,
+                      hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  const int64_t e_dim = (int64_t)L.O * L.K * L.r;
+  st = check_fuse(fuse, B, T, e_dim);
+  if (st != PG_OK) return st;
+  if (fuse->dtype != table_e_dtype(table->dtype)) return PG_EUNSUPPORTED;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!W || !out || !aligned(W, 16) || !aligned(out, 16)) return PG_EINVAL;
+  if (resid && !aligned(resid, 16)) return PG_EINVAL;
+  if (fuse->gate == PG_GATE_ENGRAM && !resid) return PG_EINVAL;
+  const int64_t e_bytes = align256(N * e_dim * elt_bytes(fuse->dtype));
+  const int64_t need = e_bytes + project_workspace(fuse, N);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PG_EINVAL;
+  void* e = workspace;
+  void* ws = static_cast<uint8_t*>(workspace) + e_bytes;
+  st = hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales, tokens,
+                                          B, T, canon_map, V, e, dev_status, stream));
+  if (st != PG_OK) return st;
+  return run_project(fuse, e, B, T, e_dim, W, resid, out, ws, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// Internal declarations shared by the library's HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/pagegram.h"
+
+namespace pg {
+
+constexpr int kMaxOrders = PG_MAX_ORDERS;
+constexpr int kMaxHeads = PG_MAX_HEADS;
+constexpr int kMaxSignWords = 4;           // r <= 256
+constexpr int kRoleStride = 5;             // c, a_0..a_3 (orders <= 4)
+constexpr int kMaxRoles = kMaxOrders * (1 + kMaxHeads + kMaxHeads * kMaxSignWords);
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+
+// Layout as the kernels see it (passed by value as a kernel argument). The
+// host fills it from a validated pg_layout; magic[] holds floor((2^64-1)/P)
+// for the exact 64-bit remainders below.
+struct DevLayout {
+  int32_t kind;       // pg_layout_kind
+  int32_t n_min;
+  int32_t O;          // number of orders
+  int32_t K;
+  int32_t r;
+  int32_t W;          // sign words per head = ceil(r/64)
+  int32_t use_signs;
+  int32_t n_roles;    // O * (1 + K + K*W)
+  uint64_t seed;
+  uint64_t pad_id;
+  uint64_t S, S_magic;
+  int64_t n_rows;
+  uint64_t P[kMaxOrders], P_magic[kMaxOrders];
+  int64_t base[kMaxOrders];
+  uint64_t Pk[kMaxOrders * kMaxHeads], Pk_magic[kMaxOrders * kMaxHeads];
+  int64_t base_k[kMaxOrders * kMaxHeads];
+};
+
+// ---------------------------------------------------------------------------
+// Integer helpers
+
+// splitmix64 output function (Steele, Lea, Flood 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// x mod P with m = floor((2^64-1)/P): q = floor(x*m / 2^64) is the true
+// quotient or one less (x*m/2^64 lies in (x/P - 1, x/P]), so one
+// conditional subtraction finishes the remainder.
+__device__ __forceinline__ uint64_t mod_magic(uint64_t x, uint64_t P, uint64_t m) {
+  uint64_t q = __umul64hi(x, m);
+  uint64_t rem = x - q * P;
+  return rem >= P ? rem - P : rem;
+}
+
+// Constants of every hash role of the layout, into LDS: role q of order i
+// is q_local = q - i*(1+K+K*W): 0 -> page hash, 1..K -> head hash k,
+// then sign word (k, w). Slot 0 is the seed word c, slots 1..4 the odd
+// multipliers a_j. Called by all threads of the block; ends with a barrier.
+__device__ inline void load_role_consts(const DevLayout& L, uint64_t* rc) {
+  const int R = 1 + L.K + L.K * L.W;
+  const int total = L.n_roles * kRoleStride;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int slot = e % kRoleStride;
+    const int q = e / kRoleStride;
+    const int i = q / R;
+    const int rr = q - i * R;
+    const int n = L.n_min + i;
+    int kind, k = 0, w = 0;
+    if (rr == 0) {
+      kind = 0;
+    } else if (rr <= L.K) {
+      kind = 1;
+      k = rr - 1;
+    } else {
+      kind = 2;
+      const int s = rr - 1 - L.K;
+      k = s / L.W;
+      w = s - k * L.W;
+    }
+    const uint64_t idx = (uint64_t)(((n * 4 + kind) * 64 + k) * 8 + w);
+    uint64_t v = mix64(L.seed + (8 * idx + slot + 1) * kGolden);
+    if (slot > 0) v |= 1ull;
+    rc[e] = v;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint64_t role_hash(const uint64_t* rc, int q,
+                                              const uint64_t* g, int n) {
+  const uint64_t* c = rc + q * kRoleStride;
+  uint64_t x = c[0];
+  for (int j = 0; j < n; ++j) x ^= g[j] * c[1 + j];
+  return mix64(x);
+}
+
+// Canonical ID of token position t of a sequence starting at `seq`
+// (pad_id when t < 0 or the token is outside [0, V)).
+__device__ __forceinline__ uint64_t canon_at(const int32_t* __restrict__ seq,
+                                             int64_t t, const int32_t* __restrict__ cmap,
+                                             int64_t V, uint64_t pad) {
+  if (t < 0) return pad;
+  const int32_t tok = seq[t];
+  if (tok < 0 || (int64_t)tok >= V) return pad;
+  return (uint64_t)(uint32_t)cmap[tok];
+}
+
+// Row of head k of order i for n-gram g (n = n_min + i), and the page for
+// PageGram (-1 otherwise). rc holds the role constants.
+__device__ __forceinline__ int64_t head_row(const DevLayout& L, const uint64_t* rc,
+                                            const uint64_t* g, int i, int k,
+                                            uint64_t* b_out, uint64_t* u_out,
+                                            int64_t* page_out) {
+  const int n = L.n_min + i;
+  const int R = 1 + L.K + L.K * L.W;
+  const uint64_t u = role_hash(rc, i * R + 1 + k, g, n);
+  *u_out = u;
+  if (L.kind == PG_PAGEGRAM) {
+    const uint64_t b = role_hash(rc, i * R, g, n);
+    const uint64_t p = mod_magic(b, L.P[i], L.P_magic[i]);
+    const uint64_t slot = mod_magic(u, L.S, L.S_magic);
+    *b_out = b;
+    *page_out = (int64_t)p;
+    return L.base[i] + (int64_t)((p * (uint64_t)L.K + (uint64_t)k) * L.S + slot);
+  }
+  *b_out = role_hash(rc, i * R, g, n);
+  *page_out = -1;
+  const int hk = i * kMaxHeads + k;
+  return L.base_k[hk] + (int64_t)mod_magic(u, L.Pk[hk], L.Pk_magic[hk]);
+}
+
+__device__ __forceinline__ uint64_t sign_word(const DevLayout& L, const uint64_t* rc,
+                                              const uint64_t* g, int i, int k, int w) {
+  if (!L.use_signs) return 0;
+  const int R = 1 + L.K + L.K * L.W;
+  return role_hash(rc, i * R + 1 + L.K + k * L.W + w, g, L.n_min + i);
+}
+
+// ---------------------------------------------------------------------------
+// Float helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files; all return hipError_t)
+
+hipError_t launch_index(const DevLayout& L, const int32_t* tokens, int64_t B, int64_t T,
+                        const int32_t* cmap, int64_t V, int32_t* canon_out,
+                        uint64_t* hash_out, int64_t* rows_out, int64_t* pages_out,
+                        uint64_t* signs_out, int32_t* status, hipStream_t s);
+
+hipError_t launch_gather(const DevLayout& L, int32_t table_dtype, const void* table,
+                         const void* scales, const int64_t* rows, const uint64_t* signs,
+                         int64_t n_tok, void* e_out, hipStream_t s);
+
+hipError_t launch_index_gather(const DevLayout& L, int32_t table_dtype, const void* table,
+                               const void* scales, const int32_t* tokens, int64_t B,
+                               int64_t T, const int32_t* cmap, int64_t V, void* e_out,
+                               int32_t* status, hipStream_t s);
+
+// Scalar-gate projection: out[N][d] = resid + g * e W^T.
+hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_t E,
+                                 const void* W, int64_t d, float g, const void* resid,
+                                 void* out, hipStream_t s);
+
+// Engram fusion (bf16): workspace layout described in engram_workspace_bytes.
+int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M);
+hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
+                         int64_t d, int64_t M, float eps, const float* gamma_h,
+                         const float* gamma_k, const float* gamma_u, const float* conv_w,
+                         int conv_k, int conv_dil, const void* h, void* out,
+                         void* workspace, int add_resid, hipStream_t s);
+
+}  // namespace pg

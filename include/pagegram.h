@@ -1,0 +1,267 @@
+/*
+ * pagegram.h -- C ABI of the MI355X (gfx950) hashed multi-head n-gram memory
+ * path: canonical IDs -> suffix n-grams -> multiply-XOR hashes -> PageGram or
+ * Engram-style rows -> gather (fp32 / bf16 / NF4), +-1 signs, concatenation
+ * -> W_V projection -> scalar-gated residual or Engram context gate with a
+ * causal depthwise conv.
+ *
+ * Sources: PageGram tech report (Empero AI, 2026-10), sections 2.1-2.3, 3.1,
+ * 3.3; Engram notes on "Conditional Memory via Scalable Lookup" (arXiv
+ * 2601.07372), sections 3.2-3.4; Engram explainer (cooking-agi), lookup
+ * pipeline and gate formulas.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers are device memory owned by the
+ *     caller, contiguous and row-major. The library allocates nothing and
+ *     keeps no pointer after it returns. There is no global mutable state.
+ *   - Work is enqueued on `stream` and the call returns without waiting;
+ *     results are visible to later work on that stream.
+ *   - Return value: PG_OK or a negative pg_status. Errors that the host can
+ *     detect (NULL required pointers, bad sizes, misalignment, unsupported
+ *     shapes) are returned before anything is enqueued. PG_EHIP means a HIP
+ *     launch failed.
+ *   - Token IDs outside [0, V) are treated as the layout's pad_id and set
+ *     bit 0 of *dev_status (an int32 in device memory, OR-ed with
+ *     atomicOr; never cleared by the library) when dev_status is non-NULL.
+ *     Every row is reduced modulo its sub-table size, so no input value can
+ *     make the gather read outside the table.
+ *   - N = B*T tokens; B rows of T tokens are separate sequences (no n-gram
+ *     and no convolution crosses a row). N = 0 is valid and enqueues nothing.
+ */
+#ifndef PAGEGRAM_H
+#define PAGEGRAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PG_API __attribute__((visibility("default")))
+#else
+#define PG_API
+#endif
+
+typedef enum pg_status {
+  PG_OK = 0,
+  PG_EINVAL = -1,        /* NULL required pointer, bad size or alignment   */
+  PG_EUNSUPPORTED = -2,  /* valid but not implemented (shape, dtype combo) */
+  PG_EHIP = -3,          /* a HIP call or kernel launch failed             */
+  PG_ERANGE = -4         /* a size overflows the library's index types     */
+} pg_status;
+
+typedef enum pg_layout_kind {
+  PG_PAGEGRAM = 0,  /* page-local heads: PageGram §3.1                      */
+  PG_ENGRAM = 1     /* one sub-table per head: PageGram §2.2, Engram §3.2    */
+} pg_layout_kind;
+
+typedef enum pg_dtype { PG_F32 = 0, PG_BF16 = 1, PG_NF4 = 2 } pg_dtype;
+
+typedef enum pg_gate {
+  PG_GATE_SCALAR = 0,  /* x <- x + g * W_V e             (PageGram §3.1)   */
+  PG_GATE_ENGRAM = 1   /* context gate + conv, M branches (Engram §3.3-3.4) */
+} pg_gate;
+
+#define PG_MAX_ORDERS 4
+#define PG_MAX_HEADS 16
+
+/*
+ * Layout of the n-gram table T in R^{R x r} and its hash functions.
+ *
+ * Orders n = n_min..n_max (1 <= n_min <= n_max <= 4); O = n_max-n_min+1.
+ * PageGram (PageGram §3.1): order n owns pages[n-n_min] = P_n pages of K*S
+ *   rows; base_n are cumulative in order of n;
+ *     p_n = b_n(x) mod P_n,
+ *     row_{n,k} = base_n + (p_n*K + k)*S + (u_{n,k}(x) mod S).
+ * Engram-style (PageGram §2.2): head (n,k) owns head_rows[n-n_min][k] =
+ *   P_{n,k} rows; bases cumulative in (n, k) order;
+ *     row_{n,k} = base_{n,k} + (u_{n,k}(x) mod P_{n,k}).
+ * The flat table of PageGram §2.1 is PG_PAGEGRAM with K=1, S=1.
+ *
+ * Hashes (hash version 1; the pages fix only "multiply-XOR"): for an n-gram
+ * g_j = canonical ID at position t-j (j = 0..n-1; pad_id before the start of
+ * the sequence) and a role (page hash b_n, head hash u_{n,k}, sign word w of
+ * head (n,k)):
+ *     h = mix64(c XOR (a_0*g_0) XOR ... XOR (a_{n-1}*g_{n-1}))   (mod 2^64)
+ * where mix64 is splitmix64's output function and, with
+ * idx = ((n*4 + kind)*64 + k)*8 + w (kind 0 page, 1 head, 2 sign),
+ *     c   = splitmix64 output 8*idx       of the stream seeded by hash_seed,
+ *     a_j = splitmix64 output 8*idx+1+j   with its low bit set.
+ * Signs (PageGram §2.1, §3.1): element j of head (n,k) is -1 when bit j%64
+ * of sign word j/64 is set, +1 otherwise; use_signs = 0 makes all signs +1.
+ *
+ * Limits: 1 <= K <= 16; S >= 1; r >= 1 with r <= 256; every P >= 1 and the
+ * total row count R < 2^62.
+ */
+typedef struct pg_layout {
+  int32_t kind;                 /* pg_layout_kind                          */
+  int32_t n_min, n_max;         /* n-gram orders                           */
+  int32_t K;                    /* heads per order                         */
+  int32_t S;                    /* slots per head per page (PageGram)      */
+  int32_t r;                    /* head row width in elements              */
+  int64_t pages[PG_MAX_ORDERS]; /* P_n (PageGram)                          */
+  int64_t head_rows[PG_MAX_ORDERS][PG_MAX_HEADS]; /* P_{n,k} (Engram-style) */
+  uint64_t hash_seed;
+  int32_t use_signs;            /* 1: hash-derived +-1 signs; 0: none      */
+  int32_t pad_id;               /* canonical ID before a sequence start;
+                                   normally the canonical vocabulary size V' */
+} pg_layout;
+
+/*
+ * Table storage (device memory, 16-byte aligned).
+ *   PG_F32 / PG_BF16: data = [n_rows][r] elements; r*elt must be a multiple
+ *     of 16 bytes.
+ *   PG_NF4 (PageGram §2.3, §3.3: 64 4-bit codes + one fp16 scale = 34 B per
+ *     64-wide row): data = [n_rows][r/2] bytes of codes, code j of a row in
+ *     byte j/2, low nibble for even j; scales = fp16 [n_rows]; r a multiple
+ *     of 32. Value = nf4[code] * scale with QLoRA's NormalFloat levels; a
+ *     page's codes (K*S*r/2 bytes) and its scales (K*S*2 bytes) are each
+ *     contiguous.
+ * n_rows must equal pg_layout_rows().
+ */
+typedef struct pg_table {
+  int32_t dtype;                /* pg_dtype                                */
+  int32_t reserved;             /* 0                                       */
+  const void* data;
+  const void* scales;           /* NF4 only, else NULL                     */
+  int64_t n_rows;
+} pg_table;
+
+/*
+ * Projection and fusion stage.
+ *   dtype: element type of e, W, the residual and the output: PG_F32 (with
+ *     an fp32 table) or PG_BF16 (bf16 or NF4 table). Accumulation is fp32.
+ *   Scalar gate (PageGram §3.1): out = resid + g * (W e), W = W_V [d x E].
+ *   Engram gate (Engram §3.3-3.4, M branches; W = [W_V; W_K^(1..M)] with
+ *   (1+M)*d rows; resid = h [M][N][d]; out [M][N][d]):
+ *     v = W_V e, k^m = W_K^(m) e,
+ *     alpha^m = sigmoid(RMSNorm_h(h^m) . RMSNorm_k(k^m) / sqrt(d)),
+ *     u^m = alpha^m v,
+ *     out^m = h^m + u^m + SiLU(CausalDWConv(RMSNorm_u(u^m))),
+ *   RMSNorm_x(z) = gamma_x * z / sqrt(mean(z^2) + eps), gains shared by the
+ *   branches; conv per channel c:
+ *     y_t[c] = sum_{j<conv_k} conv_w[c][j] * z_{t-(conv_k-1-j)*conv_dil}[c],
+ *   zero before the start of the sequence. gamma_* = fp32 [d] and conv_w =
+ *   fp32 [d][conv_k], device memory. Engram needs dtype PG_BF16, d a
+ *   multiple of 128, 1 <= M <= 8, 1 <= conv_k <= 8.
+ *   increment_only = 1 writes the increment alone (g*W e, or
+ *   u^m + SiLU(...)) without adding the residual; the Engram gate still
+ *   reads h for alpha. For the scalar gate a NULL resid acts as zero.
+ */
+typedef struct pg_fuse {
+  int32_t gate;                 /* pg_gate                                 */
+  int32_t dtype;                /* PG_F32 or PG_BF16                       */
+  int32_t d;                    /* model width (output columns per branch) */
+  int32_t M;                    /* Engram branches (ignored for scalar)    */
+  float g;                      /* scalar gate                             */
+  float eps;                    /* RMSNorm epsilon                         */
+  const float* gamma_h;
+  const float* gamma_k;
+  const float* gamma_u;
+  const float* conv_w;
+  int32_t conv_k;
+  int32_t conv_dil;
+  int32_t increment_only;       /* 0: out = resid + increment; 1: increment */
+  int32_t reserved;             /* 0                                       */
+} pg_fuse;
+
+/*
+ * pg_index -- addresses only (canonical map, n-grams, hashes, rows, signs).
+ * Touches no table, so it can run ahead of the forward (PageGram §3.3,
+ * prefetch; Engram §3.5).
+ *   tokens     int32 [B][T] (device)
+ *   canon_map  int32 [V]    (device), values < 2^31
+ *   canon_out  int32 [N]            nullable
+ *   hash_out   uint64 [N][O][1+K]   nullable: (b_n, u_{n,0..K-1})
+ *   rows_out   int64 [N][O][K]      required
+ *   pages_out  int64 [N][O]         nullable: p_n, or -1 (Engram-style)
+ *   signs_out  uint64 [N][O][K][ceil(r/64)]  required (zeros if no signs)
+ *   dev_status int32 [1]            nullable
+ */
+PG_API int pg_index(const pg_layout* layout, const int32_t* tokens, int64_t B,
+                    int64_t T, const int32_t* canon_map, int64_t V,
+                    int32_t* canon_out, uint64_t* hash_out, int64_t* rows_out,
+                    int64_t* pages_out, uint64_t* signs_out,
+                    int32_t* dev_status, hipStream_t stream);
+
+/*
+ * pg_gather -- e[t] = concat_{n, then k} s_{n,k} * deq(T[row_{n,k}(t)])
+ * (PageGram §2.2, §3.1; Engram §3.2) from pg_index's rows and signs.
+ *   rows   int64 [n_tok][O][K] (device), each in [0, n_rows)
+ *   signs  uint64 [n_tok][O][K][ceil(r/64)] (device); may be NULL only when
+ *          use_signs = 0
+ *   e_dtype PG_F32 for an fp32 table, PG_BF16 for bf16 and NF4 tables
+ *   e_out  [n_tok][O*K*r] (device, 16-byte aligned)
+ * NF4 values are fp32(nf4[code]*scale) rounded to bf16 (nearest even).
+ * Rows outside [0, n_rows) are clamped to the last row (never read out of
+ * bounds) -- pg_index never produces them.
+ */
+PG_API int pg_gather(const pg_layout* layout, const pg_table* table,
+                     const int64_t* rows, const uint64_t* signs, int64_t n_tok,
+                     int32_t e_dtype, void* e_out, hipStream_t stream);
+
+/*
+ * pg_index_gather -- pg_index followed by pg_gather in one kernel, with the
+ * rows and signs kept on chip: tokens -> e. Same arguments and results as
+ * the pair.
+ */
+PG_API int pg_index_gather(const pg_layout* layout, const pg_table* table,
+                           const int32_t* tokens, int64_t B, int64_t T,
+                           const int32_t* canon_map, int64_t V,
+                           int32_t e_dtype, void* e_out, int32_t* dev_status,
+                           hipStream_t stream);
+
+/*
+ * pg_project_gate -- projection through W and the fusion stage.
+ *   e        [N][e_dim]              (device, fuse->dtype)
+ *   W        [d_out][e_dim]          (device, fuse->dtype), d_out = d, or
+ *                                    (1+M)*d for the Engram gate
+ *   resid    x [N][d] (nullable), or h [M][N][d] (required for the
+ *            Engram gate)            (device, fuse->dtype)
+ *   out      [N][d], or [M][N][d]    (device, fuse->dtype)
+ *   workspace at least pg_workspace_size(NULL, fuse, B, T) bytes of device
+ *            memory (256-byte aligned); may be NULL when that size is 0
+ * e_dim must be a multiple of 8 (bf16) or 4 (fp32); all pointers 16-byte
+ * aligned.
+ */
+PG_API int pg_project_gate(const pg_fuse* fuse, const void* e, int64_t B,
+                           int64_t T, int64_t e_dim, const void* W,
+                           const void* resid, void* out, void* workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pg_forward -- the whole path, tokens -> out; equal to pg_index_gather
+ * followed by pg_project_gate up to float summation order. workspace at
+ * least pg_workspace_size(layout, fuse, B, T) bytes (256-byte aligned).
+ */
+PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
+                      const pg_fuse* fuse, const int32_t* tokens, int64_t B,
+                      int64_t T, const int32_t* canon_map, int64_t V,
+                      const void* W, const void* resid, void* out,
+                      void* workspace, int64_t workspace_bytes,
+                      int32_t* dev_status, hipStream_t stream);
+
+/* Message for a pg_status value (static storage). */
+PG_API const char* pg_strerror(int status);
+
+/* Hash definition version implemented (1, as described above). */
+PG_API uint32_t pg_hash_version(void);
+
+/* Total row count R of a layout; PG_EINVAL / PG_ERANGE for a bad layout. */
+PG_API int pg_layout_rows(const pg_layout* layout, int64_t* n_rows);
+
+/*
+ * Workspace bytes needed by pg_forward (layout non-NULL) or by
+ * pg_project_gate (layout NULL) for B x T tokens; negative pg_status on bad
+ * arguments.
+ */
+PG_API int64_t pg_workspace_size(const pg_layout* layout, const pg_fuse* fuse,
+                                 int64_t B, int64_t T);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEGRAM_H */
