@@ -5,13 +5,16 @@
 A step is one pass of the whole path over one batch of synthetic tokens:
 canonical map, n-grams, hashes, rows, gather/dequant/sign (pg_index_gather),
 then the W_V projection and fusion (pg_project_gate) -- the two kernels that
-pg_forward launches, called here one after the other so that HIP events can
-bracket each kernel on the stream they run on. Steps cycle through a pool of
-32 distinct token batches already resident in HBM, so the table rows of one
-step are not left in the caches by the previous one.
+pg_forward launches (checked bit for bit against pg_forward once). Steps
+cycle through a pool of 32 distinct token batches already resident in HBM, so
+the table rows of one step are not left in the caches by the previous one.
+
+The timed region is K steps back to back (wall clock and HIP events around
+it). Each kernel's launch duration is then measured the same way, K launches
+of that kernel alone between HIP events on the stream it runs on.
 
 Prints one JSON line: whole-job tokens/s, the roofline position of the
-dominant kernel (algorithmic bytes or flops per launch over its mean event
+dominant kernel (algorithmic bytes or flops per launch over its mean launch
 duration), both kernels' figures, and the CPU oracle timed on a bounded
 sample on the host cores.
 """
@@ -237,29 +240,41 @@ def main():
     same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
     del out_fwd, ws_fwd
 
-    def step(j, ev=None):
-        toks = pool[j % POOL]
-        if ev is not None:
-            ev[0].record()
-        pg.pg_index_gather(layout, table, toks, cmap, e_dtype, e)
-        if ev is not None:
-            ev[1].record()
+    def gather(j):
+        pg.pg_index_gather(layout, table, pool[j % POOL], cmap, e_dtype, e)
+
+    def project():
         pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws)
-        if ev is not None:
-            ev[2].record()
 
     for j in range(args.warmup):
-        step(j)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-              for _ in range(args.steps)]
+        gather(j)
+        project()
+    # Timed region: K whole steps back to back, no instrumentation inside.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for j in range(args.steps):
-        step(j, events[j])
+        gather(j)
+        project()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    g_ms = np.array([ev[0].elapsed_time(ev[1]) for ev in events])
-    p_ms = np.array([ev[1].elapsed_time(ev[2]) for ev in events])
+    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel launch durations: the same launches, K of each back to back
+    # between HIP events on the stream they run on.
+    def per_launch_ms(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for j in range(args.steps):
+            fn(j)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+    g_ms = np.array([per_launch_ms(gather)])
+    p_ms = np.array([per_launch_ms(lambda j: project())])
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -276,22 +291,21 @@ def main():
     g_gbps = g_bytes / (g_ms.mean() / 1e3) / 1e9
     p_peak = FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS
     p_tflops = p_flops / (p_ms.mean() / 1e3) / 1e12
-    gather = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
-              "ms_p10": float(np.percentile(g_ms, 10)), "ms_p90": float(np.percentile(g_ms, 90)),
+    gather_rec = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
               "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
               "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
               "traffic": traffic_for("gather", wl["name"])}
-    proj = {"kernel": "gemm_bf16_kernel" if act == torch.bfloat16 else "gemm_f32_kernel",
-            "ms_mean": float(p_ms.mean()), "ms_p10": float(np.percentile(p_ms, 10)),
-            "ms_p90": float(np.percentile(p_ms, 90)), "flops_per_launch": p_flops,
+    proj = {"kernel": ("gemm_bf16_pipe_kernel" if E % 32 == 0 else "gemm_bf16_kernel")
+            if act == torch.bfloat16 else "gemm_f32_kernel",
+            "ms_mean": float(p_ms.mean()), "flops_per_launch": p_flops,
             "achieved_TFLOPs": p_tflops, "frac_mfma_peak": p_tflops / p_peak,
             "bytes_per_launch": p_bytes,
             "achieved_GBps": p_bytes / (p_ms.mean() / 1e3) / 1e9,
             "traffic": traffic_for("projection", wl["name"])}
     if g_ms.mean() >= p_ms.mean():
-        roof = {"kernel": gather["kernel"], "bound": "hbm", "achieved": g_gbps,
+        roof = {"kernel": gather_rec["kernel"], "bound": "hbm", "achieved": g_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
-                "traffic": gather["traffic"]}
+                "traffic": gather_rec["traffic"]}
     else:
         roof = {"kernel": proj["kernel"], "bound": "mfma", "achieved": p_tflops,
                 "peak": p_peak, "unit": "TFLOP/s", "frac": p_tflops / p_peak,
@@ -310,7 +324,8 @@ def main():
                    "table_dtype": wl["table_dtype"], "table_rows": R, "d": wl["d"],
                    "gate": wl["gate"], "token_pool": POOL},
         "roofline": roof,
-        "gather": gather,
+        "step_ms_gpu_events": step_gpu_ms,
+        "gather": gather_rec,
         "projection": proj,
         "forward_matches_two_calls": bool(same),
         "cpu_baseline": cpu,

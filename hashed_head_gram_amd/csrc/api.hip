@@ -121,7 +121,7 @@ int check_fuse(const pg_fuse* f, int64_t B, int64_t T, int64_t e_dim) {
   if (f->dtype == PG_F32 && e_dim % 4) return PG_EUNSUPPORTED;
   if (f->gate == PG_GATE_ENGRAM) {
     if (f->dtype != PG_BF16) return PG_EUNSUPPORTED;
-    if (f->d % 128) return PG_EUNSUPPORTED;
+    if (f->d % 256 || e_dim % 64) return PG_EUNSUPPORTED;
     if (f->M < 1 || f->M > 8) return PG_EINVAL;
     if (f->conv_k < 1 || f->conv_k > 8 || f->conv_dil < 1) return PG_EINVAL;
     if ((int64_t)(f->conv_k - 1) * f->conv_dil > 64) return PG_EUNSUPPORTED;

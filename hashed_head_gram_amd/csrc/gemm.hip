@@ -1,19 +1,35 @@
 // Projection GEMMs (gfx950).
 //
-// bf16: Y[M x N] = E[M x K] . W[N x K]^T on MFMA (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation). Both operands are K-contiguous, the layout the MFMA A
-// and B fragments want. 256 threads = 4 waves in a 2 x 2 grid; each wave
-// owns a (BM/2) x (BN/2) sub-tile of 16 x 16 MFMA tiles. Tiles of BK = 64 go
-// global -> registers -> LDS (rows padded by 16 bytes) with one tile in
-// flight while the previous one is multiplied. Blocks are renumbered so that
-// each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
-// contiguous range of M-major tiles, keeping an E tile and W in its L2.
+// Y[M x N] = E[M x K] . W[N x K]^T with bf16 inputs and fp32 accumulation on
+// MFMA (v_mfma_f32_16x16x32_bf16). Both operands are K-contiguous, the layout
+// the MFMA A and B fragments take directly.
 //
-// Epilogues: the scalar gate (PageGram §3.1: x + g W_V e), and pass 1 of
+// Main kernel (K a multiple of 32): 256 threads = 4 waves in a 2 x 2 grid,
+// block tile BM x BN (256 x 192 or 256 x 256), wave tile (BM/2) x (BN/2).
+// K advances 32 at a time through a 4-stage LDS ring filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes, a
+// wave writes 1 KiB of LDS per instruction), so three K tiles are in flight
+// while one is multiplied and no VGPRs are spent on staging. Each stage
+// buffer is its own LDS object and the loop is unrolled by the ring length so
+// the compiler can tell the buffers apart; the ring is synchronised with
+// counted vmcnt waits and a bare barrier (a __syncthreads() would drain every
+// outstanding load). Within a 64-byte LDS row the four 16-byte K chunks are
+// XOR-swizzled by (row >> 1) & 3, so the 16 rows a fragment read touches fall
+// in distinct banks. Rows past M or N are clamped in-bounds for the loads and
+// never stored.
+//
+// Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
+// 8 XCDs) runs a contiguous range of M-major tiles: the N tiles of one E tile
+// run together on one XCD and share that E tile and W through its L2.
+//
+// Fallback kernel (K a multiple of 8): 128 x 128 tile, BK = 64, register-
+// staged double buffer; scalar gate only.
+//
+// Epilogues: the scalar gate (PageGram §3.1: out = x + g W_V e) and pass 1 of
 // the Engram fusion (Engram notes §3.3-3.4): v = W_V e is stored in bf16 and,
-// per token and 128-column block, the partial sums that RMSNorm and the
-// context gate need (sum v^2; per branch sum k^2, sum g_h g_k h k, sum h^2)
-// are written to the workspace, so k is never stored.
+// per token and 128-column block, the partial sums RMSNorm and the context
+// gate need (sum v^2; per branch sum k^2, sum gamma_h gamma_k h k, sum h^2)
+// go to the workspace, so k is never stored.
 //
 // fp32: a plain LDS-tiled FMA GEMM for fp32 tables (tiny workloads).
 #include "common.h"
@@ -23,10 +39,17 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;
-constexpr int kLDK = kBK + 8;   // padded LDS row (elements)
+constexpr int kColBlock = 128;   // Engram partial-sum column block
+#ifndef PIPE_BK
+#define PIPE_BK 64
+#endif
+#ifndef PIPE_STAGES
+#define PIPE_STAGES 2
+#endif
 
 enum { EPI_SCALAR = 0, EPI_ENGRAM = 1 };
 
@@ -37,8 +60,8 @@ struct EpiArgs {
   uint16_t* out;           // [M][N]
   // Engram pass 1
   int d;
-  int n_cb;                // d / BN column blocks per segment
-  const uint16_t* h;       // [Mbr][M][d] or NULL
+  int n_cb;                // d / 128 column blocks per segment
+  const uint16_t* h;       // [Mbr][M][d]
   uint16_t* v;             // [M][d]
   float* part_v;           // [n_cb][M]
   float* part_k;           // [Mbr][3][n_cb][M]
@@ -50,7 +73,354 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-template <int BM, int BN, int EPI>
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One direct global->LDS load: each lane moves 16 bytes from `src`; the wave
+// writes 1 KiB at LDS byte address `lds` (wave-uniform, passed in M0) +
+// 16 * lane. Issued as inline asm without a memory clobber, so the compiler's
+// wait-count pass neither tracks it nor waits for it before LDS reads (its
+// LDS-DMA tracking would otherwise wait for every outstanding load). The ring
+// orders it explicitly: counted vmcnt waits, then a barrier fenced on both
+// sides by compiler-only memory barriers; volatile asm keeps its order.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+__device__ __forceinline__ int64_t remap_block(int64_t bid, int64_t total) {
+  const int64_t per = total / 8;
+  if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  return bid;
+}
+
+// Tile of a (renumbered) block id: groups of kGroupM M tiles, each group
+// walked N-major, so the blocks running together on an XCD share a few E
+// tiles and a few W tiles instead of one E tile and all of W.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void block_tile(int64_t id, int64_t nbm, int64_t nbn, int64_t* bm,
+                                           int64_t* bn) {
+  const int64_t per_group = (int64_t)kGroupM * nbn;
+  const int64_t g = id / per_group;
+  const int64_t local = id - g * per_group;
+  const int64_t rows = nbm - g * kGroupM < kGroupM ? nbm - g * kGroupM : kGroupM;
+  *bn = local / rows;
+  *bm = g * kGroupM + (local - *bn * rows);
+}
+
+// Scalar-gate epilogue for a wave's FM x FN accumulator tiles.
+template <int FM, int FN>
+__device__ __forceinline__ void epi_scalar(const f32x4_t (&acc)[FM][FN], int64_t row0,
+                                           int col0, int lane, int64_t M, int N,
+                                           const EpiArgs& ep) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = row0 + i * 16 + 4 * (lane >> 4) + q;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 16 + (lane & 15);
+        if (col >= N) continue;
+        const int64_t o = row * N + col;
+        const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
+        ep.out[o] = f32_to_bf16(x + ep.g * acc[i][j][q]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel
+
+// LDS bytes of the K ring and of the epilogue's staging tile.
+template <int BM, int BN, int BK, int S>
+struct PipeCfg {
+  static constexpr int kStageBytes = (BM + BN) * BK * 2;
+  static constexpr int kRingBytes = S * kStageBytes;
+  static constexpr int kPad = 4;                 // floats of row padding
+  static constexpr int kRowStride = BN + kPad;   // staged accumulator row (floats)
+  // rows of the block tile staged per epilogue pass: as many wave rows
+  // (BM/2) as fit beside nothing else (the ring is dead by then)
+  static constexpr int kPassRows =
+      (BM / 2) * kRowStride * 4 <= kRingBytes ? BM / 2 : BM / 4;
+  static constexpr int kStageTileBytes = kPassRows * kRowStride * 4;
+  static constexpr int kLdsBytes = kRingBytes > kStageTileBytes ? kRingBytes : kStageTileBytes;
+};
+
+template <int BM, int BN, int BK, int S, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, int64_t M, int N,
+    int K, EpiArgs ep) {
+  using Cfg = PipeCfg<BM, BN, BK, S>;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int LPR = BK / 8;                  // 16-byte chunks (lanes) per row
+  constexpr int RPI = 64 / LPR;                // rows per DMA instruction
+  constexpr int ROWS_PER_LINE = 64 / BK;       // rows per 128-byte LDS line
+  constexpr int A_DMA = BM / RPI / 4;          // DMA instructions per wave per stage
+  constexpr int B_DMA = BN / RPI / 4;
+  constexpr int L = A_DMA + B_DMA;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile split");
+  static_assert((S - 1) * L < 64, "vmcnt range");
+  static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t nbm = (M + BM - 1) / BM;
+  const int64_t nbn = (N + BN - 1) / BN;
+  int64_t bm, bn;
+  block_tile(remap_block(blockIdx.x, nbm * nbn), nbm, nbn, &bm, &bn);
+  const int64_t m0 = bm * BM;
+  const int n0 = (int)(bn * BN);
+
+  // Residual tile, fetched at the start so its latency overlaps the first
+  // K tiles (scalar gate, N a multiple of 8): chunk q of this thread is
+  // epilogue item tid + 256 q (row-major 8-column chunks of the block tile).
+  constexpr int XCH = EPI == EPI_SCALAR ? BM * BN / 8 / kThreads : 1;
+  uint4 xpre[XCH];
+  const bool xvec = EPI == EPI_SCALAR && ep.resid != nullptr && (N & 7) == 0;
+  if constexpr (EPI == EPI_SCALAR) {
+#pragma unroll
+    for (int q = 0; q < XCH; ++q) {
+      const int idx = tid + q * kThreads;
+      const int64_t row = m0 + idx / (BN / 8);
+      const int col = n0 + (idx % (BN / 8)) * 8;
+      xpre[q] = make_uint4(0, 0, 0, 0);
+      if (xvec && row < M && col < N)
+        xpre[q] = *reinterpret_cast<const uint4*>(ep.resid + row * N + col);
+    }
+  }
+
+  // Swizzle of the 16-byte chunk position within a row: rows sharing a
+  // 128-byte line, and the next lines, rotate their chunks.
+  auto swz = [](int r) { return (r / ROWS_PER_LINE) & (LPR - 1); };
+
+  // DMA: lane covers row lane / LPR of an RPI-row slab and LDS chunk position
+  // lane % LPR, loading the logical chunk pos ^ swz(row).
+  const int dr = lane / LPR;
+  const int dpos = lane % LPR;
+  const uint16_t* a_src[A_DMA];
+  const uint16_t* b_src[B_DMA];
+#pragma unroll
+  for (int j = 0; j < A_DMA; ++j) {
+    const int r = (wave * A_DMA + j) * RPI + dr;
+    int64_t gm = m0 + r;
+    gm = gm < M ? gm : M - 1;
+    a_src[j] = A + gm * (int64_t)K + ((dpos ^ swz(r)) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < B_DMA; ++j) {
+    const int r = (wave * B_DMA + j) * RPI + dr;
+    int gn = n0 + r;
+    gn = gn < N ? gn : N - 1;
+    b_src[j] = Bw + (int64_t)gn * K + ((dpos ^ swz(r)) * 8);
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int kt) {
+    const int k0 = kt * BK;
+    const uint32_t st = lds0 + (kt % S) * Cfg::kStageBytes;
+    const uint32_t la = st + wave * A_DMA * 1024;
+    const uint32_t lb = st + BM * BK * 2 + wave * B_DMA * 1024;
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) dma16(a_src[j] + k0, la + j * 1024);
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) dma16(b_src[j] + k0, lb + j * 1024);
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Fragment read: lane reads row (lane & 15) of a 16-row tile, logical chunk
+  // ks * 4 + (lane >> 4), stored at that chunk ^ swz(row).
+  const int fr = lane & 15;
+  auto compute = [&](int kt) {
+    const uint16_t* sa = reinterpret_cast<const uint16_t*>(smem + (kt % S) * Cfg::kStageBytes);
+    const uint16_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int pos = ((ks * 4 + (lane >> 4)) ^ swz(fr)) * 8;
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &sa[(wm * WTM + i * 16 + fr) * BK + pos]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &sb[(wn * WTN + j * 16 + fr) * BK + pos]));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue(s);
+  for (int kt = 0; kt < KT; ++kt) {
+    // Wait for this wave's loads of stage kt (later stages may stay in
+    // flight), then for everyone's; the barrier also retires the reads of
+    // stage kt-1, whose buffer the next issue overwrites.
+    const int ahead = KT - 1 - kt;
+    if (ahead >= S - 2)
+      wait_vmcnt<(S - 2) * L>();
+    else if (S > 3 && ahead == 2)
+      wait_vmcnt<2 * L>();
+    else if (S > 2 && ahead == 1)
+      wait_vmcnt<L>();
+    else
+      wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + S - 1 < KT) issue(kt + S - 1);
+    compute(kt);
+  }
+
+  // Epilogue: stage the accumulators through LDS, kPassRows rows at a time,
+  // so global traffic is 16-byte loads and stores along rows.
+  float* tile = reinterpret_cast<float*>(smem);
+  constexpr int R = Cfg::kPassRows;
+  constexpr int RS = Cfg::kRowStride;
+  constexpr int CPR = BN / 8;                   // 8-column chunks per row
+  constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
+  static_assert(R * CPR % kThreads == 0, "epilogue items");
+#pragma unroll
+  for (int p = 0; p < BM / R; ++p) {
+    asm volatile("" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rl = wm * WTM + i * 16 + 4 * (lane >> 4) + q - p * R;
+        if (rl < 0 || rl >= R) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          tile[rl * RS + wn * WTN + j * 16 + (lane & 15)] = acc[i][j][q];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * kThreads;
+      const int rl = idx / CPR;
+      const int c8 = (idx - rl * CPR) * 8;
+      const int64_t row = m0 + p * R + rl;
+      const int col = n0 + c8;
+      const float4 lo = *reinterpret_cast<const float4*>(&tile[rl * RS + c8]);
+      const float4 hi = *reinterpret_cast<const float4*>(&tile[rl * RS + c8 + 4]);
+      float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if constexpr (EPI == EPI_SCALAR) {
+        if (row >= M) continue;
+        if (col + 8 <= N && (N & 7) == 0) {
+          const int64_t o = row * N + col;
+          float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (xvec) {
+            const uint4 xr = xpre[p * ITEMS + it];
+            const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              x[2 * u] = bf16_to_f32((uint16_t)(xw[u] & 0xFFFFu));
+              x[2 * u + 1] = bf16_to_f32((uint16_t)(xw[u] >> 16));
+            }
+          }
+          uint32_t ow[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            ow[u] = (uint32_t)f32_to_bf16(x[2 * u] + ep.g * y[2 * u]) |
+                    ((uint32_t)f32_to_bf16(x[2 * u + 1] + ep.g * y[2 * u + 1]) << 16);
+          *reinterpret_cast<uint4*>(ep.out + o) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        } else {
+          for (int u = 0; u < 8 && col + u < N; ++u) {
+            const int64_t o = row * N + col + u;
+            const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
+            ep.out[o] = f32_to_bf16(x + ep.g * y[u]);
+          }
+        }
+      } else {
+        // Engram pass 1: the block's columns lie in one segment (BN divides
+        // d); 16 consecutive lanes hold one row's 128-column block.
+        const bool live = row < M;
+        const int seg = col / ep.d;
+        const int c = col - seg * ep.d;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        if (seg == 0) {
+          uint32_t vw[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            vw[u] = (uint32_t)f32_to_bf16(y[2 * u]) | ((uint32_t)f32_to_bf16(y[2 * u + 1]) << 16);
+          if (live)
+            *reinterpret_cast<uint4*>(ep.v + row * ep.d + c) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s0 += y[u] * y[u];
+        } else {
+          const int br = seg - 1;
+          float hv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (live) {
+            const uint4 hr = *reinterpret_cast<const uint4*>(ep.h + ((int64_t)br * M + row) * ep.d + c);
+            const uint32_t hw[4] = {hr.x, hr.y, hr.z, hr.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              hv[2 * u] = bf16_to_f32((uint16_t)(hw[u] & 0xFFFFu));
+              hv[2 * u + 1] = bf16_to_f32((uint16_t)(hw[u] >> 16));
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            s0 += y[u] * y[u];
+            s1 += ep.gamma_h[c + u] * ep.gamma_k[c + u] * hv[u] * y[u];
+            s2 += hv[u] * hv[u];
+          }
+        }
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) {
+          s0 += __shfl_xor(s0, sh, 64);
+          s1 += __shfl_xor(s1, sh, 64);
+          s2 += __shfl_xor(s2, sh, 64);
+        }
+        if (live && (lane & 15) == 0) {
+          const int cb = c / kColBlock;
+          if (seg == 0) {
+            ep.part_v[(int64_t)cb * M + row] = s0;
+          } else {
+            float* pk = ep.part_k + (int64_t)(seg - 1) * 3 * ep.n_cb * M;
+            pk[((int64_t)0 * ep.n_cb + cb) * M + row] = s0;
+            pk[((int64_t)1 * ep.n_cb + cb) * M + row] = s1;
+            pk[((int64_t)2 * ep.n_cb + cb) * M + row] = s2;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fallback kernel (K % 8 == 0), scalar gate
+
+constexpr int kBK = 64;
+constexpr int kLDK = kBK + 8;   // padded LDS row (elements)
+
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, int64_t M, int N,
     int K, EpiArgs ep) {
@@ -68,10 +438,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
   const int64_t nbm = (M + BM - 1) / BM;
   const int64_t nbn = (N + BN - 1) / BN;
-  const int64_t total = nbm * nbn;
-  int64_t bid = blockIdx.x;
-  const int64_t per = total / 8;
-  if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  const int64_t bid = remap_block(blockIdx.x, nbm * nbn);
   const int64_t bm = bid / nbn;
   const int64_t bn = bid - bm * nbn;
   const int64_t m0 = bm * BM;
@@ -142,97 +509,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     if (kt + 1 < KT) sstore(cur ^ 1);
     __syncthreads();
   }
-
-  // Accumulator element (i, j, q) is row wm*WTM + i*16 + 4*(lane/16) + q,
-  // column wn*WTN + j*16 + lane%16 of the block tile.
-  if constexpr (EPI == EPI_SCALAR) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + q;
-        if (row >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WTN + j * 16 + (lane & 15);
-          if (col >= N) continue;
-          const int64_t o = row * N + col;
-          const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
-          ep.out[o] = f32_to_bf16(x + ep.g * acc[i][j][q]);
-        }
-      }
-  } else {
-    // Engram pass 1. BN divides d, so the tile lies in one segment:
-    // s = 0 is v = W_V e, s = 1 + m is k^m = W_K^(m) e.
-    __shared__ float red[2][BM][3];
-    const int seg = n0 / ep.d;
-    const int c0 = n0 - seg * ep.d;   // first column of the tile in its segment
-    const int cb = c0 / BN;
-    const int br = seg - 1;
-    float s0[FM][4], s1[FM][4], s2[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s0[i][q] = 0.f;
-        s1[i][q] = 0.f;
-        s2[i][q] = 0.f;
-        const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + q;
-        if (row >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int c = c0 + wn * WTN + j * 16 + (lane & 15);
-          const float y = acc[i][j][q];
-          if (seg == 0) {
-            ep.v[row * ep.d + c] = f32_to_bf16(y);
-            s0[i][q] += y * y;
-          } else {
-            const float hv = ep.h ? bf16_to_f32(ep.h[((int64_t)br * M + row) * ep.d + c]) : 0.f;
-            s0[i][q] += y * y;
-            s1[i][q] += ep.gamma_h[c] * ep.gamma_k[c] * hv * y;
-            s2[i][q] += hv * hv;
-          }
-        }
-      }
-    // Reduce over the 16 lanes that share rows, then over the two wave columns.
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int sh = 1; sh < 16; sh <<= 1) {
-          s0[i][q] += __shfl_xor(s0[i][q], sh, 64);
-          s1[i][q] += __shfl_xor(s1[i][q], sh, 64);
-          s2[i][q] += __shfl_xor(s2[i][q], sh, 64);
-        }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rl = wm * WTM + i * 16 + 4 * (lane >> 4) + q;
-          red[wn][rl][0] = s0[i][q];
-          red[wn][rl][1] = s1[i][q];
-          red[wn][rl][2] = s2[i][q];
-        }
-    }
-    __syncthreads();
-    for (int rl = tid; rl < BM; rl += kThreads) {
-      const int64_t row = m0 + rl;
-      if (row >= M) continue;
-      const float a0 = red[0][rl][0] + red[1][rl][0];
-      if (seg == 0) {
-        ep.part_v[(int64_t)cb * M + row] = a0;
-      } else {
-        const float a1 = red[0][rl][1] + red[1][rl][1];
-        const float a2 = red[0][rl][2] + red[1][rl][2];
-        float* pk = ep.part_k + (int64_t)br * 3 * ep.n_cb * M;
-        pk[((int64_t)0 * ep.n_cb + cb) * M + row] = a0;
-        pk[((int64_t)1 * ep.n_cb + cb) * M + row] = a1;
-        pk[((int64_t)2 * ep.n_cb + cb) * M + row] = a2;
-      }
-    }
-  }
+  epi_scalar<FM, FN>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, M, N, ep);
 }
 
 // fp32: 64 x 64 tile, BK = 16, each thread a 4 x 4 block of outputs.
@@ -284,6 +561,17 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
   }
 }
 
+template <int BM, int BN, int EPI>
+hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
+                       const EpiArgs& ep, hipStream_t s) {
+  constexpr int BK = PIPE_BK, S = PIPE_STAGES;
+  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
+                     static_cast<const uint16_t*>(W), M, N, K, ep);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_t E,
@@ -296,39 +584,43 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
                        (int)E, g, static_cast<const float*>(resid), static_cast<float*>(out));
     return hipGetLastError();
   }
-  constexpr int BM = 128, BN = 128;
   EpiArgs ep{};
   ep.g = g;
   ep.resid = static_cast<const uint16_t*>(resid);
   ep.out = static_cast<uint16_t*>(out);
+  if (E % PIPE_BK == 0) {
+    // Pick the N tile by rounds of 256 concurrent blocks times block work.
+    auto cost = [&](int64_t bn) {
+      const int64_t blocks = ((N + 255) / 256) * ((d + bn - 1) / bn);
+      return ((blocks + 255) / 256) * bn;
+    };
+    if (cost(192) < cost(256))
+      return launch_pipe<256, 192, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+    return launch_pipe<256, 256, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+  }
+  constexpr int BM = 128, BN = 128;
   const int64_t blocks = ((N + BM - 1) / BM) * ((d + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_SCALAR>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
-                     static_cast<const uint16_t*>(W), N, (int)d, (int)E, ep);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), N,
+                     (int)d, (int)E, ep);
   return hipGetLastError();
 }
 
-// Engram pass 1 (declared in engram.hip's launcher).
+// Engram pass 1 (E % 32 == 0 and d % 256 == 0, checked by the caller).
 hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
                                int64_t d, int64_t Mbr, const void* h,
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
                                float* part_v, float* part_k, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
   EpiArgs ep{};
   ep.d = (int)d;
-  ep.n_cb = (int)(d / BN);
+  ep.n_cb = (int)(d / kColBlock);
   ep.h = static_cast<const uint16_t*>(h);
   ep.v = v;
   ep.part_v = part_v;
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
-  const int64_t Ntot = (1 + Mbr) * d;
-  const int64_t blocks = ((N + BM - 1) / BM) * (Ntot / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_ENGRAM>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
-                     static_cast<const uint16_t*>(W), N, (int)Ntot, (int)E, ep);
-  return hipGetLastError();
+  return launch_pipe<128, 256, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
 }
 
 }  // namespace pg

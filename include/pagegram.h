@@ -145,7 +145,8 @@ typedef struct pg_table {
  *     y_t[c] = sum_{j<conv_k} conv_w[c][j] * z_{t-(conv_k-1-j)*conv_dil}[c],
  *   zero before the start of the sequence. gamma_* = fp32 [d] and conv_w =
  *   fp32 [d][conv_k], device memory. Engram needs dtype PG_BF16, d a
- *   multiple of 128, 1 <= M <= 8, 1 <= conv_k <= 8.
+ *   multiple of 256, e_dim a multiple of 64, 1 <= M <= 8, 1 <= conv_k <= 8
+ *   and (conv_k-1)*conv_dil <= 64.
  *   increment_only = 1 writes the increment alone (g*W e, or
  *   u^m + SiLU(...)) without adding the residual; the Engram gate still
  *   reads h for alpha. For the scalar gate a NULL resid acts as zero.
