@@ -1,4 +1,5 @@
-// Engram fusion, pass 2 (gfx950), after the projection GEMM's pass 1.
+// Engram fusion after the projection GEMM's pass 1 (gfx950): a per-token gate
+// kernel, then pass 2.
 //
 // Engram notes §3.3-3.4 with M branches sharing v = W_V e:
 //   alpha^m_t = sigmoid(RMSNorm_h(h^m_t) . RMSNorm_k(k^m_t) / sqrt(d))
@@ -6,14 +7,15 @@
 //   z^m_t     = RMSNorm_u(u^m_t) = gamma_u * v_t * alpha / sqrt(alpha^2 ms(v_t) + eps)
 //   out^m_t   = h^m_t + u^m_t + SiLU(sum_j w_j * z^m_{t-(kw-1-j)*dil})
 // From pass 1 the workspace holds v (bf16) and per-token partial sums over
-// 128-column blocks: sum v^2, and per branch sum k^2, sum gamma_h gamma_k h k,
+// 256-column blocks: sum v^2, and per branch sum k^2, sum gamma_h gamma_k h k,
 // sum h^2. RMSNorm_h(h).RMSNorm_k(k) = that dot / (rms(h) rms(k)).
 //
-// A block takes TB tokens of one sequence and 256 channels. It first turns
-// the partial sums into (alpha, z-scale) per token and branch for its tokens
-// and the (kw-1)*dil tokens before them, stages that v window in LDS, then
-// each lane produces 8 channels of one token for all branches with 16-byte
-// loads of h and stores of out.
+// The gate kernel reduces those partials once per (branch, token) into alpha
+// and the RMSNorm_u scale alpha / sqrt(alpha^2 mean(v^2) + eps). Pass 2 takes
+// TB tokens of one sequence and 256 channels per block, stages the v window
+// (its tokens and the (kw-1)*dil before them) and their gate values in LDS,
+// and each lane produces 8 channels of one token for all branches with
+// 16-byte loads of h and stores of out.
 #include "common.h"
 
 namespace pg {
@@ -28,32 +30,56 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTB = 32;          // tokens per block
 constexpr int kCB = 256;         // channels per block
-constexpr int kMaxHalo = 64;     // (conv_k - 1) * conv_dil
-constexpr int kMaxBr = 8;
-constexpr int kMaxTaps = 8;
-constexpr int kColBlock = 128;   // pass-1 column block of the partial sums
+constexpr int kColBlock = 256;   // pass-1 column block of the partial sums
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// gate[m][0][tok] = alpha, gate[m][1][tok] = alpha / sqrt(alpha^2 ms(v) + eps).
+__global__ __launch_bounds__(kThreads) void engram_gate_kernel(
+    int64_t N, int d, int Mbr, float eps, const float* __restrict__ part_v,
+    const float* __restrict__ part_k, int n_cb, float* __restrict__ gate) {
+  const int64_t tok = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int m = blockIdx.y;
+  if (tok >= N) return;
+  const float inv_d = 1.0f / (float)d;
+  float sv = 0.f, sk = 0.f, dot = 0.f, sh = 0.f;
+  const float* pk = part_k + (int64_t)m * 3 * n_cb * N;
+  for (int cb = 0; cb < n_cb; ++cb) {
+    sv += part_v[(int64_t)cb * N + tok];
+    sk += pk[((int64_t)0 * n_cb + cb) * N + tok];
+    dot += pk[((int64_t)1 * n_cb + cb) * N + tok];
+    sh += pk[((int64_t)2 * n_cb + cb) * N + tok];
+  }
+  const float rk = 1.0f / sqrtf(sk * inv_d + eps);
+  const float rh = 1.0f / sqrtf(sh * inv_d + eps);
+  const float zlogit = dot * rh * rk / sqrtf((float)d);
+  const float alpha = 1.0f / (1.0f + expf(-zlogit));
+  gate[((int64_t)m * 2 + 0) * N + tok] = alpha;
+  gate[((int64_t)m * 2 + 1) * N + tok] = alpha / sqrtf(alpha * alpha * (sv * inv_d) + eps);
+}
+
+// Dynamic LDS: v window [(TB + H) x 256] bf16, then alpha and the RMSNorm_u
+// scale [M][TB + H] fp32.
+template <int KW>
 __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
-    int64_t T, int d, int Mbr, float eps, const float* __restrict__ gamma_u,
-    const float* __restrict__ conv_w, int kw, int dil, const uint16_t* __restrict__ v,
-    const float* __restrict__ part_v, const float* __restrict__ part_k, int n_cb,
-    int64_t N, const uint16_t* __restrict__ h, uint16_t* __restrict__ out, int add_resid) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[(kTB + kMaxHalo) * kCB];
-  __shared__ float alphaL[kMaxBr][kTB + kMaxHalo];
-  __shared__ float facL[kMaxBr][kTB + kMaxHalo];
+    int64_t T, int d, int Mbr, const float* __restrict__ gamma_u,
+    const float* __restrict__ conv_w, int dil, const uint16_t* __restrict__ v,
+    const float* __restrict__ gate, int64_t N, const uint16_t* __restrict__ h,
+    uint16_t* __restrict__ out, int add_resid) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  constexpr int kw = KW;
+  const int H = (kw - 1) * dil;
+  const int rowsL = kTB + H;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(dsm);
+  float* alphaS = reinterpret_cast<float*>(dsm + rowsL * kCB * 2);
+  float* facS = alphaS + Mbr * rowsL;
 
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kTB;
   const int c0 = blockIdx.z * kCB;
-  const int H = (kw - 1) * dil;
-  const int rowsL = kTB + H;
   const int tid = threadIdx.x;
-  const float inv_d = 1.0f / (float)d;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
-  // Per-token scalars for positions t0-H .. t0+TB-1 (LDS index tau - (t0-H)).
+  // Gate values for positions t0-H .. t0+TB-1 (LDS index tau - (t0-H)).
   for (int q = tid; q < rowsL * Mbr; q += kThreads) {
     const int m = q / rowsL;
     const int tl = q - m * rowsL;
@@ -61,22 +87,11 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
     float alpha = 0.f, fac = 0.f;
     if (tau >= 0 && tau < T) {
       const int64_t tok = b * T + tau;
-      float sv = 0.f, sk = 0.f, dot = 0.f, sh = 0.f;
-      const float* pk = part_k + (int64_t)m * 3 * n_cb * N;
-      for (int cb = 0; cb < n_cb; ++cb) {
-        sv += part_v[(int64_t)cb * N + tok];
-        sk += pk[((int64_t)0 * n_cb + cb) * N + tok];
-        dot += pk[((int64_t)1 * n_cb + cb) * N + tok];
-        sh += pk[((int64_t)2 * n_cb + cb) * N + tok];
-      }
-      const float rk = 1.0f / sqrtf(sk * inv_d + eps);
-      const float rh = 1.0f / sqrtf(sh * inv_d + eps);
-      const float zlogit = dot * rh * rk * inv_sqrt_d;
-      alpha = 1.0f / (1.0f + expf(-zlogit));
-      fac = alpha / sqrtf(alpha * alpha * (sv * inv_d) + eps);
+      alpha = gate[((int64_t)m * 2 + 0) * N + tok];
+      fac = gate[((int64_t)m * 2 + 1) * N + tok];
     }
-    alphaL[m][tl] = alpha;
-    facL[m][tl] = fac;
+    alphaS[m * rowsL + tl] = alpha;
+    facS[m * rowsL + tl] = fac;
   }
   // v window [t0-H, t0+TB) x [c0, c0+256), zeros outside the sequence.
   for (int q = tid; q < rowsL * (kCB / 8); q += kThreads) {
@@ -93,13 +108,13 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
   const int cg = tid & 31;
   const int c = c0 + cg * 8;
   if (c >= d) return;
-  float w[8][kMaxTaps];
+  float w[8][kw];
   float gu[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     gu[x] = gamma_u[c + x];
 #pragma unroll
-    for (int j = 0; j < kMaxTaps; ++j) w[x][j] = j < kw ? conv_w[(c + x) * kw + j] : 0.f;
+    for (int j = 0; j < kw; ++j) w[x][j] = conv_w[(c + x) * kw + j];
   }
   for (int tl = tid >> 5; tl < kTB; tl += kThreads / 32) {
     const int64_t t = t0 + tl;
@@ -117,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
     }
     for (int m = 0; m < Mbr; ++m) {
       float conv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int j = 0; j < kw; ++j) {
         const int lj = li - (kw - 1 - j) * dil;   // >= 0; zero rows before the start
-        const float f = facL[m][lj];
+        const float f = facS[m * rowsL + lj];
         const uint4 raw = *reinterpret_cast<const uint4*>(&vt[lj * kCB + cg * 8]);
         const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -129,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
               w[2 * x + 1][j] * (gu[2 * x + 1] * bf16_to_f32((uint16_t)(ws[x] >> 16)) * f);
         }
       }
-      const float alpha = alphaL[m][li];
+      const float alpha = alphaS[m * rowsL + li];
       const int64_t o = ((int64_t)m * N + b * T + t) * d + c;
       float hv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (add_resid) {
@@ -160,7 +176,8 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
 
 int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M) {
   const int64_t n_cb = d / kColBlock;
-  return align256(N * d * 2) + align256(n_cb * N * 4) + align256(M * 3 * n_cb * N * 4);
+  return align256(N * d * 2) + align256(n_cb * N * 4) + align256(M * 3 * n_cb * N * 4) +
+         align256(M * 2 * N * 4);
 }
 
 hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
@@ -174,13 +191,34 @@ hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const v
   auto* v = reinterpret_cast<uint16_t*>(base);
   auto* part_v = reinterpret_cast<float*>(base + align256(N * d * 2));
   auto* part_k = reinterpret_cast<float*>(base + align256(N * d * 2) + align256(n_cb * N * 4));
+  auto* gate = reinterpret_cast<float*>(base + align256(N * d * 2) + align256(n_cb * N * 4) +
+                                        align256(M * 3 * n_cb * N * 4));
   hipError_t err = launch_engram_pass1(e, N, E, W, d, M, h, gamma_h, gamma_k, v, part_v,
                                        part_k, s);
   if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(engram_gate_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads),
+                                              (unsigned)M),
+                     dim3(kThreads), 0, s, N, (int)d, (int)M, eps, part_v, part_k, (int)n_cb,
+                     gate);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   dim3 grid((unsigned)((T + kTB - 1) / kTB), (unsigned)B, (unsigned)((d + kCB - 1) / kCB));
-  hipLaunchKernelGGL(engram_pass2_kernel, grid, dim3(kThreads), 0, s, T, (int)d, (int)M, eps,
-                     gamma_u, conv_w, conv_k, conv_dil, v, part_v, part_k, (int)n_cb, N,
-                     static_cast<const uint16_t*>(h), static_cast<uint16_t*>(out), add_resid);
+  const int rowsL = kTB + (conv_k - 1) * conv_dil;
+  const size_t lds = (size_t)rowsL * kCB * 2 + (size_t)2 * M * rowsL * 4;
+  const auto* hh = static_cast<const uint16_t*>(h);
+  auto* oo = static_cast<uint16_t*>(out);
+#define PG_PASS2(KW)                                                                       \
+  case KW:                                                                                 \
+    hipLaunchKernelGGL(engram_pass2_kernel<KW>, grid, dim3(kThreads), lds, s, T, (int)d,   \
+                       (int)M, gamma_u, conv_w, conv_dil, v, gate, N, hh, oo, add_resid); \
+    break;
+  switch (conv_k) {
+    PG_PASS2(1) PG_PASS2(2) PG_PASS2(3) PG_PASS2(4) PG_PASS2(5) PG_PASS2(6) PG_PASS2(7)
+    PG_PASS2(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef PG_PASS2
   return hipGetLastError();
 }
 

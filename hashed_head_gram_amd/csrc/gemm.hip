@@ -43,7 +43,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kColBlock = 128;   // Engram partial-sum column block
+constexpr int kColBlock = 256;   // Engram partial-sum column block
 #ifndef PIPE_BK
 #define PIPE_BK 64
 #endif
@@ -60,7 +60,7 @@ struct EpiArgs {
   uint16_t* out;           // [M][N]
   // Engram pass 1
   int d;
-  int n_cb;                // d / 128 column blocks per segment
+  int n_cb;                // d / 256 column blocks per segment
   const uint16_t* h;       // [Mbr][M][d]
   uint16_t* v;             // [M][d]
   float* part_v;           // [n_cb][M]
@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile split");
   static_assert((S - 1) * L < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
+  static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLdsBytes];
 
@@ -187,22 +188,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   const int64_t m0 = bm * BM;
   const int n0 = (int)(bn * BN);
 
-  // Residual tile, fetched at the start so its latency overlaps the first
-  // K tiles (scalar gate, N a multiple of 8): chunk q of this thread is
+  // The epilogue's bf16 input tile -- the residual x (scalar gate, N a
+  // multiple of 8) or h of this branch (Engram k tiles) -- is fetched at the
+  // start so its latency overlaps the first K tiles. Chunk q of this thread is
   // epilogue item tid + 256 q (row-major 8-column chunks of the block tile).
-  constexpr int XCH = EPI == EPI_SCALAR ? BM * BN / 8 / kThreads : 1;
-  uint4 xpre[XCH];
-  const bool xvec = EPI == EPI_SCALAR && ep.resid != nullptr && (N & 7) == 0;
+  constexpr int CPR = BN / 8;                   // 8-column chunks per row
+  constexpr int PCH = BM * BN / 8 / kThreads;
+  uint4 pre[PCH];
+  bool pre_ok;
+  const uint16_t* pre_src;
+  int64_t pre_ld;
+  int pre_c0;
   if constexpr (EPI == EPI_SCALAR) {
+    pre_ok = ep.resid != nullptr && (N & 7) == 0;
+    pre_src = ep.resid;
+    pre_ld = N;
+    pre_c0 = n0;
+  } else {
+    const int seg = n0 / ep.d;
+    pre_ok = seg > 0;
+    pre_src = seg > 0 ? ep.h + (int64_t)(seg - 1) * M * ep.d : ep.h;
+    pre_ld = ep.d;
+    pre_c0 = n0 - seg * ep.d;
+  }
 #pragma unroll
-    for (int q = 0; q < XCH; ++q) {
-      const int idx = tid + q * kThreads;
-      const int64_t row = m0 + idx / (BN / 8);
-      const int col = n0 + (idx % (BN / 8)) * 8;
-      xpre[q] = make_uint4(0, 0, 0, 0);
-      if (xvec && row < M && col < N)
-        xpre[q] = *reinterpret_cast<const uint4*>(ep.resid + row * N + col);
-    }
+  for (int q = 0; q < PCH; ++q) {
+    const int idx = tid + q * kThreads;
+    const int64_t row = m0 + idx / CPR;
+    const int cc = (idx % CPR) * 8;
+    pre[q] = make_uint4(0, 0, 0, 0);
+    if (pre_ok && row < M && n0 + cc < N)
+      pre[q] = *reinterpret_cast<const uint4*>(pre_src + row * pre_ld + pre_c0 + cc);
   }
 
   // Swizzle of the 16-byte chunk position within a row: rows sharing a
@@ -302,7 +318,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   float* tile = reinterpret_cast<float*>(smem);
   constexpr int R = Cfg::kPassRows;
   constexpr int RS = Cfg::kRowStride;
-  constexpr int CPR = BN / 8;                   // 8-column chunks per row
   constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
   static_assert(R * CPR % kThreads == 0, "epilogue items");
 #pragma unroll
@@ -329,27 +344,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
       const int col = n0 + c8;
       const float4 lo = *reinterpret_cast<const float4*>(&tile[rl * RS + c8]);
       const float4 hi = *reinterpret_cast<const float4*>(&tile[rl * RS + c8 + 4]);
-      float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float xin[8];
+      {
+        const uint4 pr = pre[p * ITEMS + it];
+        const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          xin[2 * u] = bf16_to_f32((uint16_t)(pw[u] & 0xFFFFu));
+          xin[2 * u + 1] = bf16_to_f32((uint16_t)(pw[u] >> 16));
+        }
+      }
       if constexpr (EPI == EPI_SCALAR) {
         if (row >= M) continue;
-        if (col + 8 <= N && (N & 7) == 0) {
-          const int64_t o = row * N + col;
-          float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (xvec) {
-            const uint4 xr = xpre[p * ITEMS + it];
-            const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              x[2 * u] = bf16_to_f32((uint16_t)(xw[u] & 0xFFFFu));
-              x[2 * u + 1] = bf16_to_f32((uint16_t)(xw[u] >> 16));
-            }
-          }
+        if (pre_ok || (ep.resid == nullptr && col + 8 <= N && (N & 7) == 0)) {
+          if (col >= N) continue;
           uint32_t ow[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            ow[u] = (uint32_t)f32_to_bf16(x[2 * u] + ep.g * y[2 * u]) |
-                    ((uint32_t)f32_to_bf16(x[2 * u + 1] + ep.g * y[2 * u + 1]) << 16);
-          *reinterpret_cast<uint4*>(ep.out + o) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+            ow[u] = (uint32_t)f32_to_bf16(xin[2 * u] + ep.g * y[2 * u]) |
+                    ((uint32_t)f32_to_bf16(xin[2 * u + 1] + ep.g * y[2 * u + 1]) << 16);
+          *reinterpret_cast<uint4*>(ep.out + row * N + col) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
         } else {
           for (int u = 0; u < 8 && col + u < N; ++u) {
             const int64_t o = row * N + col + u;
@@ -358,8 +373,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
           }
         }
       } else {
-        // Engram pass 1: the block's columns lie in one segment (BN divides
-        // d); 16 consecutive lanes hold one row's 128-column block.
+        // Engram pass 1: the block's 256 columns are one partial-sum column
+        // block of one segment (BN = 256 divides d); the 32 consecutive lanes
+        // of a row hold it.
         const bool live = row < M;
         const int seg = col / ep.d;
         const int c = col - seg * ep.d;
@@ -374,31 +390,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
 #pragma unroll
           for (int u = 0; u < 8; ++u) s0 += y[u] * y[u];
         } else {
-          const int br = seg - 1;
-          float hv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (live) {
-            const uint4 hr = *reinterpret_cast<const uint4*>(ep.h + ((int64_t)br * M + row) * ep.d + c);
-            const uint32_t hw[4] = {hr.x, hr.y, hr.z, hr.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              hv[2 * u] = bf16_to_f32((uint16_t)(hw[u] & 0xFFFFu));
-              hv[2 * u + 1] = bf16_to_f32((uint16_t)(hw[u] >> 16));
-            }
-          }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             s0 += y[u] * y[u];
-            s1 += ep.gamma_h[c + u] * ep.gamma_k[c + u] * hv[u] * y[u];
-            s2 += hv[u] * hv[u];
+            s1 += ep.gamma_h[c + u] * ep.gamma_k[c + u] * xin[u] * y[u];
+            s2 += xin[u] * xin[u];
           }
         }
 #pragma unroll
-        for (int sh = 1; sh < 16; sh <<= 1) {
+        for (int sh = 1; sh < CPR; sh <<= 1) {
           s0 += __shfl_xor(s0, sh, 64);
           s1 += __shfl_xor(s1, sh, 64);
           s2 += __shfl_xor(s2, sh, 64);
         }
-        if (live && (lane & 15) == 0) {
+        if (live && (lane % CPR) == 0) {
           const int cb = c / kColBlock;
           if (seg == 0) {
             ep.part_v[(int64_t)cb * M + row] = s0;
@@ -620,7 +625,7 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
-  return launch_pipe<128, 256, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
+  return launch_pipe<256, 256, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
 }
 
 }  // namespace pg

@@ -192,9 +192,10 @@ def test_project_and_forward_validation():
                      gamma_k=FAKE, gamma_u=FAKE, conv_w=FAKE)
     need = pg.pg_workspace_size(None, g, 2, 64)
     N = 128
-    n_cb = 2560 // 128
+    n_cb = 2560 // 256
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == a(N * 2560 * 2) + a(n_cb * N * 4) + a(4 * 3 * n_cb * N * 4)
+    assert need == (a(N * 2560 * 2) + a(n_cb * N * 4) + a(4 * 3 * n_cb * N * 4)
+                    + a(4 * 2 * N * 4))
     assert L.pg_project_gate(by(g), FAKE, 2, 64, 1280, FAKE, FAKE, FAKE, FAKE,
                              need - 1, None) == pg.PG_EINVAL
     assert L.pg_project_gate(by(g), FAKE, 2, 64, 1280, FAKE, None, FAKE, FAKE,
