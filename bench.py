@@ -2,16 +2,17 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one pass of the whole path over one batch of synthetic tokens:
-canonical map, n-grams, hashes, rows, gather/dequant/sign (pg_index_gather),
-then the W_V projection and fusion (pg_project_gate) -- the two kernels that
-pg_forward launches (checked bit for bit against pg_forward once). Steps
-cycle through a pool of 32 distinct token batches already resident in HBM, so
-the table rows of one step are not left in the caches by the previous one.
+A step is one pg_forward call over one batch of synthetic tokens: canonical
+map, n-grams, hashes, rows, gather/dequant/sign, concatenation, W_V
+projection and fusion. Steps cycle through a pool of 32 distinct token
+batches already resident in HBM, so the table rows of one step are not left
+in the caches by the previous one.
 
 The timed region is K steps back to back (wall clock and HIP events around
 it). Each kernel's launch duration is then measured the same way, K launches
-of that kernel alone between HIP events on the stream it runs on.
+of that stage's entry point alone between HIP events on the stream it runs
+on: pg_index_gather and pg_project_gate, the two calls pg_forward makes
+(checked bit for bit once).
 
 Prints one JSON line: whole-job tokens/s, the roofline position of the
 dominant kernel (algorithmic bytes or flops per launch over its mean launch
@@ -223,46 +224,40 @@ def main():
         resid = torch.empty(N, wl["d"], dtype=act, device=dev)
         out = torch.empty(N, wl["d"], dtype=act, device=dev)
     sdev.fill_normal(resid, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
+    ws = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8, device=dev)
+    # pg_forward's constituents, for per-kernel timing.
     e = torch.empty(N, E, dtype=act, device=dev)
-    ws = torch.empty(max(pg.pg_workspace_size(None, fuse, B, T), 256), dtype=torch.uint8,
-                     device=dev)
-    ws_fwd = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8,
-                         device=dev)
+    ws2 = torch.empty_like(ws)
     torch.cuda.synchronize()
 
-    # pg_forward launches exactly these two kernels; check once that the
-    # two-call step reproduces it bit for bit.
+    def forward(j):
+        pg.pg_forward(layout, table, fuse, pool[j % POOL], cmap, W, resid, out, ws)
+
+    # The stage calls reproduce pg_forward bit for bit.
     out_fwd = torch.empty_like(out)
-    pg.pg_forward(layout, table, fuse, pool[0], cmap, W, resid, out_fwd, ws_fwd)
+    forward(0)
+    out_fwd.copy_(out)
     pg.pg_index_gather(layout, table, pool[0], cmap, e_dtype, e)
-    pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws)
+    pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws2)
     torch.cuda.synchronize()
     same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
-    del out_fwd, ws_fwd
-
-    def gather(j):
-        pg.pg_index_gather(layout, table, pool[j % POOL], cmap, e_dtype, e)
-
-    def project():
-        pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws)
+    del out_fwd
 
     for j in range(args.warmup):
-        gather(j)
-        project()
-    # Timed region: K whole steps back to back, no instrumentation inside.
+        forward(j)
+    # Timed region: K whole steps (pg_forward) back to back.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for j in range(args.steps):
-        gather(j)
-        project()
+        forward(j)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # Per-kernel launch durations: the same launches, K of each back to back
+    # Per-kernel launch durations: K launches of each stage back to back
     # between HIP events on the stream they run on.
     def per_launch_ms(fn):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -273,8 +268,10 @@ def main():
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps
-    g_ms = np.array([per_launch_ms(gather)])
-    p_ms = np.array([per_launch_ms(lambda j: project())])
+    g_ms = np.array([per_launch_ms(lambda j: pg.pg_index_gather(
+        layout, table, pool[j % POOL], cmap, e_dtype, e))])
+    p_ms = np.array([per_launch_ms(lambda j: pg.pg_project_gate(
+        fuse, e, B, T, W, resid, out, ws2))])
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -292,9 +289,9 @@ def main():
     p_peak = FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS
     p_tflops = p_flops / (p_ms.mean() / 1e3) / 1e12
     gather_rec = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
-              "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
-              "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
-              "traffic": traffic_for("gather", wl["name"])}
+                  "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
+                  "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
+                  "traffic": traffic_for("gather", wl["name"])}
     proj = {"kernel": ("gemm_bf16_pipe_kernel" if E % 32 == 0 else "gemm_bf16_kernel")
             if act == torch.bfloat16 else "gemm_f32_kernel",
             "ms_mean": float(p_ms.mean()), "flops_per_launch": p_flops,
@@ -302,6 +299,8 @@ def main():
             "bytes_per_launch": p_bytes,
             "achieved_GBps": p_bytes / (p_ms.mean() / 1e3) / 1e9,
             "traffic": traffic_for("projection", wl["name"])}
+    stages = {"pg_index_gather_ms": float(g_ms.mean()),
+              "pg_project_gate_ms": float(p_ms.mean())}
     if g_ms.mean() >= p_ms.mean():
         roof = {"kernel": gather_rec["kernel"], "bound": "hbm", "achieved": g_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
@@ -325,9 +324,10 @@ def main():
                    "gate": wl["gate"], "token_pool": POOL},
         "roofline": roof,
         "step_ms_gpu_events": step_gpu_ms,
+        "stages": stages,
         "gather": gather_rec,
         "projection": proj,
-        "forward_matches_two_calls": bool(same),
+        "forward_matches_stage_calls": bool(same),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -6,7 +6,7 @@
 //
 // Main kernel (K a multiple of 32): 256 threads = 4 waves in a 2 x 2 grid,
 // block tile BM x BN (256 x 192 or 256 x 256), wave tile (BM/2) x (BN/2).
-// K advances 32 at a time through a 4-stage LDS ring filled by direct
+// K advances BK = 64 at a time through LDS rings filled by direct
 // global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes, a
 // wave writes 1 KiB of LDS per instruction), so three K tiles are in flight
 // while one is multiplied and no VGPRs are spent on staging. Each stage
@@ -144,8 +144,12 @@ __device__ __forceinline__ void epi_scalar(const f32x4_t (&acc)[FM][FN], int64_t
 // LDS bytes of the K ring and of the epilogue's staging tile.
 template <int BM, int BN, int BK, int S>
 struct PipeCfg {
-  static constexpr int kStageBytes = (BM + BN) * BK * 2;
-  static constexpr int kRingBytes = S * kStageBytes;
+  // E ring of S buffers (E tiles S-1 stages ahead) and W ring of 2 buffers
+  // (one stage ahead): E comes from further away (MALL/HBM) than W (L2).
+  static constexpr int kABytes = BM * BK * 2;
+  static constexpr int kBBytes = BN * BK * 2;
+  static constexpr int kBOffset = S * kABytes;
+  static constexpr int kRingBytes = S * kABytes + 2 * kBBytes;
   static constexpr int kPad = 4;                 // floats of row padding
   static constexpr int kRowStride = BN + kPad;   // staged accumulator row (floats)
   // rows of the block tile staged per epilogue pass: as many wave rows
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   constexpr int L = A_DMA + B_DMA;
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile split");
-  static_assert((S - 1) * L < 64, "vmcnt range");
+  static_assert(S == 2 || S == 3, "E ring of 2 or 3 buffers");
+  static_assert(L + A_DMA < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
   static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
 
@@ -211,15 +216,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
     pre_ld = ep.d;
     pre_c0 = n0 - seg * ep.d;
   }
-#pragma unroll
-  for (int q = 0; q < PCH; ++q) {
+  // Chunks fetched at the start; the rest are fetched when the epilogue
+  // begins (the 256 x 256 tile has no registers for all of them in the loop).
+  constexpr int PEARLY = BM * BN > 256 * 192 ? PCH / 2 : PCH;
+  auto fetch_pre = [&](int q) {
     const int idx = tid + q * kThreads;
     const int64_t row = m0 + idx / CPR;
     const int cc = (idx % CPR) * 8;
     pre[q] = make_uint4(0, 0, 0, 0);
     if (pre_ok && row < M && n0 + cc < N)
       pre[q] = *reinterpret_cast<const uint4*>(pre_src + row * pre_ld + pre_c0 + cc);
-  }
+  };
+#pragma unroll
+  for (int q = 0; q < PEARLY; ++q) fetch_pre(q);
 
   // Swizzle of the 16-byte chunk position within a row: rows sharing a
   // 128-byte line, and the next lines, rotate their chunks.
@@ -246,15 +255,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
     b_src[j] = Bw + (int64_t)gn * K + ((dpos ^ swz(r)) * 8);
   }
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int kt) {
-    const int k0 = kt * BK;
-    const uint32_t st = lds0 + (kt % S) * Cfg::kStageBytes;
-    const uint32_t la = st + wave * A_DMA * 1024;
-    const uint32_t lb = st + BM * BK * 2 + wave * B_DMA * 1024;
+  auto issue_a = [&](int kt) {
+    const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j) dma16(a_src[j] + k0, la + j * 1024);
+    for (int j = 0; j < A_DMA; ++j) dma16(a_src[j] + kt * BK, la + j * 1024);
+  };
+  auto issue_b = [&](int kt) {
+    const uint32_t lb = lds0 + Cfg::kBOffset + (kt & 1) * Cfg::kBBytes + wave * B_DMA * 1024;
 #pragma unroll
-    for (int j = 0; j < B_DMA; ++j) dma16(b_src[j] + k0, lb + j * 1024);
+    for (int j = 0; j < B_DMA; ++j) dma16(b_src[j] + kt * BK, lb + j * 1024);
   };
 
   f32x4_t acc[FM][FN];
@@ -267,8 +276,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   // ks * 4 + (lane >> 4), stored at that chunk ^ swz(row).
   const int fr = lane & 15;
   auto compute = [&](int kt) {
-    const uint16_t* sa = reinterpret_cast<const uint16_t*>(smem + (kt % S) * Cfg::kStageBytes);
-    const uint16_t* sb = sa + BM * BK;
+    const uint16_t* sa = reinterpret_cast<const uint16_t*>(smem + (kt % S) * Cfg::kABytes);
+    const uint16_t* sb =
+        reinterpret_cast<const uint16_t*>(smem + Cfg::kBOffset + (kt & 1) * Cfg::kBBytes);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int pos = ((ks * 4 + (lane >> 4)) ^ swz(fr)) * 8;
@@ -290,26 +300,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   };
 
   const int KT = K / BK;
+  // Issue order: W(kt+1) then E(kt+S-1) each step, after W(0), E(0..S-2).
+  // The wait at step kt needs E(kt) and W(kt); with S = 3 the only load
+  // issued after W(kt) is E(kt+1), which may stay in flight.
+  issue_b(0);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue(s);
+    if (s < KT) issue_a(s);
   for (int kt = 0; kt < KT; ++kt) {
-    // Wait for this wave's loads of stage kt (later stages may stay in
-    // flight), then for everyone's; the barrier also retires the reads of
-    // stage kt-1, whose buffer the next issue overwrites.
-    const int ahead = KT - 1 - kt;
-    if (ahead >= S - 2)
-      wait_vmcnt<(S - 2) * L>();
-    else if (S > 3 && ahead == 2)
-      wait_vmcnt<2 * L>();
-    else if (S > 2 && ahead == 1)
-      wait_vmcnt<L>();
+    if (S == 3 && kt + 1 < KT)
+      wait_vmcnt<(S == 3 ? A_DMA : 0)>();
     else
       wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + S - 1 < KT) issue(kt + S - 1);
+    // buffers refilled here were last read by compute(kt - 1)
+    if (kt + 1 < KT) issue_b(kt + 1);
+    if (kt + S - 1 < KT) issue_a(kt + S - 1);
     compute(kt);
   }
 
@@ -320,6 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   constexpr int RS = Cfg::kRowStride;
   constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
   static_assert(R * CPR % kThreads == 0, "epilogue items");
+#pragma unroll
+  for (int q = PEARLY; q < PCH; ++q) fetch_pre(q);
 #pragma unroll
   for (int p = 0; p < BM / R; ++p) {
     asm volatile("" ::: "memory");

@@ -139,14 +139,20 @@ def test_forward_within_tolerance(i):
 
 @pytest.mark.parametrize("i", range(5))
 def test_forward_equals_stage_composition(i):
+    # pg_forward == pg_index_gather -> pg_project_gate == pg_index -> pg_gather
+    # -> pg_project_gate, bit for bit (same products, same summation order).
     c = case(i)
     out = c.run_forward()
     e = c.run_index_gather()
     out2 = c.run_project(e)
+    idx = c.run_index()
+    e3 = c.e_buffer()
+    pg.pg_gather(c.layout, c.table, idx["rows"], idx["signs"], c.e_dtype, e3)
+    out3 = c.run_project(e3)
     again = c.run_forward()
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16) if c.act == torch.bfloat16 else out,
-                       out2.view(torch.int16) if c.act == torch.bfloat16 else out2)
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+    assert torch.equal(out.view(torch.uint8), out3.view(torch.uint8))
     # run-to-run determinism
     assert torch.equal(out.view(torch.uint8), again.view(torch.uint8))
 
