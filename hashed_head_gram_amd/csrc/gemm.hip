@@ -39,16 +39,16 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kColBlock = 256;   // Engram partial-sum column block
-#ifndef PIPE_BK
-#define PIPE_BK 64
-#endif
-#ifndef PIPE_STAGES
-#define PIPE_STAGES 2
+constexpr int kPipeBK = 64;      // K stage of the pipelined kernel
+constexpr int kPipeStages = 2;   // its LDS ring
+#ifndef GEMM_CFG
+#define GEMM_CFG 0
 #endif
 
 enum { EPI_SCALAR = 0, EPI_ENGRAM = 1 };
@@ -69,6 +69,16 @@ struct EpiArgs {
   const float* gamma_k;
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even) in one instruction
+// (v_cvt_pk_bf16_f32); `a` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
@@ -88,8 +98,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // LDS-DMA tracking would otherwise wait for every outstanding load). The ring
 // orders it explicitly: counted vmcnt waits, then a barrier fenced on both
 // sides by compiler-only memory barriers; volatile asm keeps its order.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds));
+// The address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit
+// byte offset, so a stage's loads hold one VGPR per lane instead of a 64-bit
+// pointer per instruction.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -133,7 +146,7 @@ __device__ __forceinline__ void epi_scalar(const f32x4_t (&acc)[FM][FN], int64_t
         if (col >= N) continue;
         const int64_t o = row * N + col;
         const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
-        ep.out[o] = f32_to_bf16(x + ep.g * acc[i][j][q]);
+        ep.out[o] = (uint16_t)pack_bf16x2(x + ep.g * acc[i][j][q], 0.f);
       }
     }
 }
@@ -144,12 +157,11 @@ __device__ __forceinline__ void epi_scalar(const f32x4_t (&acc)[FM][FN], int64_t
 // LDS bytes of the K ring and of the epilogue's staging tile.
 template <int BM, int BN, int BK, int S>
 struct PipeCfg {
-  // E ring of S buffers (E tiles S-1 stages ahead) and W ring of 2 buffers
-  // (one stage ahead): E comes from further away (MALL/HBM) than W (L2).
+  // rings of S buffers for the E and the W tiles (S - 1 stages in flight)
   static constexpr int kABytes = BM * BK * 2;
   static constexpr int kBBytes = BN * BK * 2;
   static constexpr int kBOffset = S * kABytes;
-  static constexpr int kRingBytes = S * kABytes + 2 * kBBytes;
+  static constexpr int kRingBytes = S * (kABytes + kBBytes);
   static constexpr int kPad = 4;                 // floats of row padding
   static constexpr int kRowStride = BN + kPad;   // staged accumulator row (floats)
   // rows of the block tile staged per epilogue pass: as many wave rows
@@ -160,23 +172,24 @@ struct PipeCfg {
   static constexpr int kLdsBytes = kRingBytes > kStageTileBytes ? kRingBytes : kStageTileBytes;
 };
 
-template <int BM, int BN, int BK, int S, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
+template <int BM, int BN, int BK, int S, int EPI, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, int64_t M, int N,
     int K, EpiArgs ep) {
   using Cfg = PipeCfg<BM, BN, BK, S>;
   constexpr int WTM = BM / 2, WTN = BN / 2;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA tiles per wave
   constexpr int LPR = BK / 8;                  // 16-byte chunks (lanes) per row
   constexpr int RPI = 64 / LPR;                // rows per DMA instruction
   constexpr int ROWS_PER_LINE = 64 / BK;       // rows per 128-byte LDS line
   constexpr int A_DMA = BM / RPI / 4;          // DMA instructions per wave per stage
   constexpr int B_DMA = BN / RPI / 4;
   constexpr int L = A_DMA + B_DMA;
-  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BK == 32 || BK == 64, "K stage of 32 or 64");
+  static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
+  static_assert(2 * L < 64, "vmcnt range");
   static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile split");
-  static_assert(S == 2 || S == 3, "E ring of 2 or 3 buffers");
-  static_assert(L + A_DMA < 64, "vmcnt range");
+  static_assert(L < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
   static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
 
@@ -194,12 +207,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
   const int n0 = (int)(bn * BN);
 
   // The epilogue's bf16 input tile -- the residual x (scalar gate, N a
-  // multiple of 8) or h of this branch (Engram k tiles) -- is fetched at the
-  // start so its latency overlaps the first K tiles. Chunk q of this thread is
-  // epilogue item tid + 256 q (row-major 8-column chunks of the block tile).
+  // multiple of 8) or h of this branch (Engram k tiles). Chunk q of this
+  // thread is epilogue item tid + 256 q (row-major 8-column chunks of the
+  // block tile); each epilogue pass fetches its own chunks before staging
+  // the accumulators, so the loads overlap the LDS round trip and the main
+  // loop keeps its registers for the fragment pipeline.
   constexpr int CPR = BN / 8;                   // 8-column chunks per row
-  constexpr int PCH = BM * BN / 8 / kThreads;
-  uint4 pre[PCH];
   bool pre_ok;
   const uint16_t* pre_src;
   int64_t pre_ld;
@@ -216,19 +229,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
     pre_ld = ep.d;
     pre_c0 = n0 - seg * ep.d;
   }
-  // Chunks fetched at the start; the rest are fetched when the epilogue
-  // begins (the 256 x 256 tile has no registers for all of them in the loop).
-  constexpr int PEARLY = BM * BN > 256 * 192 ? PCH / 2 : PCH;
-  auto fetch_pre = [&](int q) {
-    const int idx = tid + q * kThreads;
-    const int64_t row = m0 + idx / CPR;
-    const int cc = (idx % CPR) * 8;
-    pre[q] = make_uint4(0, 0, 0, 0);
-    if (pre_ok && row < M && n0 + cc < N)
-      pre[q] = *reinterpret_cast<const uint4*>(pre_src + row * pre_ld + pre_c0 + cc);
-  };
-#pragma unroll
-  for (int q = 0; q < PEARLY; ++q) fetch_pre(q);
 
   // Swizzle of the 16-byte chunk position within a row: rows sharing a
   // 128-byte line, and the next lines, rotate their chunks.
@@ -236,165 +236,286 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
 
   // DMA: lane covers row lane / LPR of an RPI-row slab and LDS chunk position
   // lane % LPR, loading the logical chunk pos ^ swz(row).
+  // Each instruction covers the RPI-row group g = wave * X_DMA + j; the
+  // group's first row (clamped to the last valid row) is the scalar base and
+  // rows past the matrix repeat its last row (never stored).
   const int dr = lane / LPR;
   const int dpos = lane % LPR;
-  const uint16_t* a_src[A_DMA];
-  const uint16_t* b_src[B_DMA];
-#pragma unroll
-  for (int j = 0; j < A_DMA; ++j) {
-    const int r = (wave * A_DMA + j) * RPI + dr;
-    int64_t gm = m0 + r;
-    gm = gm < M ? gm : M - 1;
-    a_src[j] = A + gm * (int64_t)K + ((dpos ^ swz(r)) * 8);
-  }
-#pragma unroll
-  for (int j = 0; j < B_DMA; ++j) {
-    const int r = (wave * B_DMA + j) * RPI + dr;
-    int gn = n0 + r;
-    gn = gn < N ? gn : N - 1;
-    b_src[j] = Bw + (int64_t)gn * K + ((dpos ^ swz(r)) * 8);
-  }
+  // (a group's first row is a multiple of RPI, so swz(row) = swz(dr))
+  const uint32_t chunk_b = (uint32_t)((dpos ^ swz(dr)) * 16);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_a = [&](int kt) {
+  auto issue_rows = [&](const uint16_t* mat, int64_t rows, int64_t r0, int kt, uint32_t lds) {
+    int64_t rb = r0 < rows ? r0 : rows - 1;
+    const int lim = (int)(rows - 1 - rb);
+    const int rr = dr < lim ? dr : lim;
+    dma16(mat + rb * K + kt * BK, (uint32_t)(rr * K * 2) + chunk_b, lds);
+  };
+  auto issue_a_part = [&](int kt, int j0, int j1) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j) dma16(a_src[j] + kt * BK, la + j * 1024);
+    for (int j = j0; j < j1; ++j)
+      issue_rows(A, M, m0 + (wave * A_DMA + j) * RPI, kt, la + j * 1024);
   };
-  auto issue_b = [&](int kt) {
-    const uint32_t lb = lds0 + Cfg::kBOffset + (kt & 1) * Cfg::kBBytes + wave * B_DMA * 1024;
+  auto issue_b_part = [&](int kt, int j0, int j1) {
+    const uint32_t lb = lds0 + Cfg::kBOffset + (kt % S) * Cfg::kBBytes + wave * B_DMA * 1024;
 #pragma unroll
-    for (int j = 0; j < B_DMA; ++j) dma16(b_src[j] + kt * BK, lb + j * 1024);
+    for (int j = j0; j < j1; ++j)
+      issue_rows(Bw, N, n0 + (wave * B_DMA + j) * RPI, kt, lb + j * 1024);
   };
+  auto issue_a = [&](int kt) { issue_a_part(kt, 0, A_DMA); };
+  auto issue_b = [&](int kt) { issue_b_part(kt, 0, B_DMA); };
 
-  f32x4_t acc[FM][FN];
+  f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // Fragment read: lane reads row (lane & 15) of a 16-row tile, logical chunk
-  // ks * 4 + (lane >> 4), stored at that chunk ^ swz(row).
-  const int fr = lane & 15;
-  auto compute = [&](int kt) {
+  // v_mfma_f32_32x32x16_bf16: lane l holds A row l % 32 (B column l % 32),
+  // K elements 8 (l / 32) .. +7 of the 16; D element q of lane l is row
+  // 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32. (On gfx950 this form
+  // sustains far more of the bf16 peak than the 16 x 16 x 32 one.)
+  const int fr = lane & 31;
+  // Fragments of K step s (16 wide, s = 0..3) of stage kt: logical 16-byte
+  // chunk 2 s + lane / 32 of row fr of each 32-row tile, stored at that
+  // chunk ^ swz(row).
+  auto load_frags = [&](int kt, int st, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
     const uint16_t* sa = reinterpret_cast<const uint16_t*>(smem + (kt % S) * Cfg::kABytes);
     const uint16_t* sb =
-        reinterpret_cast<const uint16_t*>(smem + Cfg::kBOffset + (kt & 1) * Cfg::kBBytes);
+        reinterpret_cast<const uint16_t*>(smem + Cfg::kBOffset + (kt % S) * Cfg::kBBytes);
+    const int pos = ((st * 2 + (lane >> 5)) ^ swz(fr)) * 8;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int pos = ((ks * 4 + (lane >> 4)) ^ swz(fr)) * 8;
-      bf16x8_t af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i)
+      af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[(wm * WTM + i * 32 + fr) * BK + pos]));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &sa[(wm * WTM + i * 16 + fr) * BK + pos]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &sb[(wn * WTN + j * 16 + fr) * BK + pos]));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < FN; ++j)
+      bf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sb[(wn * WTN + j * 32 + fr) * BK + pos]));
   };
-
-  const int KT = K / BK;
-  // Issue order: W(kt+1) then E(kt+S-1) each step, after W(0), E(0..S-2).
-  // The wait at step kt needs E(kt) and W(kt); with S = 3 the only load
-  // issued after W(kt) is E(kt+1), which may stay in flight.
-  issue_b(0);
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue_a(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (S == 3 && kt + 1 < KT)
-      wait_vmcnt<(S == 3 ? A_DMA : 0)>();
-    else
-      wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // buffers refilled here were last read by compute(kt - 1)
-    if (kt + 1 < KT) issue_b(kt + 1);
-    if (kt + S - 1 < KT) issue_a(kt + S - 1);
-    compute(kt);
-  }
-
-  // Epilogue: stage the accumulators through LDS, kPassRows rows at a time,
-  // so global traffic is 16-byte loads and stores along rows.
-  float* tile = reinterpret_cast<float*>(smem);
-  constexpr int R = Cfg::kPassRows;
-  constexpr int RS = Cfg::kRowStride;
-  constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
-  static_assert(R * CPR % kThreads == 0, "epilogue items");
-#pragma unroll
-  for (int q = PEARLY; q < PCH; ++q) fetch_pre(q);
-#pragma unroll
-  for (int p = 0; p < BM / R; ++p) {
-    asm volatile("" ::: "memory");
-    __syncthreads();
+  auto mma = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rl = wm * WTM + i * 16 + 4 * (lane >> 4) + q - p * R;
-        if (rl < 0 || rl >= R) continue;
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  auto block_sync = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Two-buffer rings for E and W: stage kt+1 is loaded while stage kt is
+  // multiplied. The barrier at the top of step kt means stage kt is in LDS
+  // and every wave is done reading stage kt-1, whose buffers then take
+  // stage kt+1.
+  // Rings of S buffers: stage kt+S-1 is loaded while stage kt is multiplied.
+  // The barrier at the top of step kt means stage kt is in LDS and every wave
+  // is done reading stage kt-1, whose buffers then take stage kt+S-1. Within
+  // a stage the fragment reads of K step st+1 go out one after each MFMA of
+  // step st (LDS latency hides behind issued matrix work), and the loads of
+  // stage kt+S-1 are spread over the steps so that the wave never stalls on a
+  // burst of load issues while the matrix pipe idles.
+  const int KT = K / BK;
+  constexpr int PD = S - 1;                     // stages in flight
+  constexpr int NS = BK / 16;                   // K steps per stage
+  constexpr int RD = FM + FN;                   // fragment reads per step
+  static_assert(FM * FN >= RD, "reads interleave with the step's MFMAs");
+#pragma unroll
+  for (int st = 0; st < PD; ++st)
+    if (st < KT) {
+      issue_b(st);
+      issue_a(st);
+    }
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads of stage kt are done when at most the later issued
+    // stages (up to PD - 1 of them) are outstanding
+    const int later = KT - 1 - kt < PD - 1 ? KT - 1 - kt : PD - 1;
+    if (later >= 2)
+      wait_vmcnt<2 * L>();
+    else if (later == 1)
+      wait_vmcnt<L>();
+    else
+      wait_vmcnt<0>();
+    block_sync();
+    const bool more = kt + PD < KT;
+    bf16x8_t fa[NS][FM], fb[NS][FN];
+    load_frags(kt, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (st + 1 < NS) load_frags(kt, st + 1, fa[st + 1], fb[st + 1]);
+      mma(fa[st], fb[st]);
+      if (st == 0) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      if (st + 1 < NS) {
+#pragma unroll
+        for (int q = 0; q < RD; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - RD, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+      }
+      if (more) {
+        issue_a_part(kt + PD, st * A_DMA / NS, (st + 1) * A_DMA / NS);
+        issue_b_part(kt + PD, st * B_DMA / NS, (st + 1) * B_DMA / NS);
+      }
+    }
+  }
+
+  // Epilogue: stage the accumulators through LDS, kPassRows rows at a time,
+  // so global traffic is 16-byte loads and stores along rows. The passes
+  // synchronise with LDS-only barriers: a __syncthreads() would also wait
+  // for the previous pass's global stores. The scalar gate fetches its whole
+  // residual tile before the first store (the fragment registers are free
+  // by then), so no load is ever waited for behind a store.
+  float* tile = reinterpret_cast<float*>(smem);
+  constexpr int R = Cfg::kPassRows;
+  constexpr int RS = Cfg::kRowStride;
+  constexpr int NP = BM / R;                    // passes
+  constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
+  static_assert(R * CPR % kThreads == 0, "epilogue items");
+  auto lds_barrier = [] {
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // A full tile (every row and column inside, N a multiple of 8) takes the
+  // branch-free path; edge tiles check each element.
+  const bool full = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
+  uint4 pre[NP * ITEMS];
+  if (pre_ok && full) {
+#pragma unroll
+    for (int q = 0; q < NP * ITEMS; ++q) {
+      const int idx = tid + q * kThreads;
+      pre[q] = *reinterpret_cast<const uint4*>(pre_src + (m0 + idx / CPR) * pre_ld + pre_c0 +
+                                               (idx % CPR) * 8);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NP * ITEMS; ++q) pre[q] = make_uint4(0, 0, 0, 0);
+  }
+  // Engram: this thread's 8 columns are the same in every item (CPR divides
+  // the thread count), so the gain products are read once.
+  float gg[8];
+  if constexpr (EPI == EPI_ENGRAM) {
+    static_assert(kThreads % CPR == 0, "every item of a thread has the same columns");
+    const int seg = n0 / ep.d;
+    const int c = n0 - seg * ep.d + (tid % CPR) * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gg[u] = seg > 0 ? ep.gamma_h[c + u] * ep.gamma_k[c + u] : 0.f;
+  }
+  // Pass p: the accumulator rows [p R, p R + R) of the block tile go to LDS.
+  auto stage = [&](int p) {
+    lds_barrier();
+    static_assert(R % 32 == 0, "a pass holds whole 32-row MFMA tiles");
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      // wave-uniform: is this wave's 32-row tile i in pass p?
+      if ((wm * WTM + i * 32) / R != p) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rl = wm * WTM + i * 32 + (q >> 2) * 8 + 4 * (lane >> 5) + (q & 3) - p * R;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          tile[rl * RS + wn * WTN + j * 16 + (lane & 15)] = acc[i][j][q];
+          tile[rl * RS + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][q];
       }
-    __syncthreads();
+    }
+    lds_barrier();
+  };
+  // Item it of pass p: tile row rl = (tid + 256 it) / CPR, columns c8..c8+7.
+  auto item_y = [&](int p, int it, float (&y)[8], float (&xin)[8]) {
+    const int idx = tid + it * kThreads;
+    const int rl = idx / CPR;
+    const int c8 = (idx - rl * CPR) * 8;
+    const float4 lo = *reinterpret_cast<const float4*>(&tile[rl * RS + c8]);
+    const float4 hi = *reinterpret_cast<const float4*>(&tile[rl * RS + c8 + 4]);
+    y[0] = lo.x; y[1] = lo.y; y[2] = lo.z; y[3] = lo.w;
+    y[4] = hi.x; y[5] = hi.y; y[6] = hi.z; y[7] = hi.w;
+    const uint4 pr = pre[p * ITEMS + it];
+    const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int idx = tid + it * kThreads;
-      const int rl = idx / CPR;
-      const int c8 = (idx - rl * CPR) * 8;
-      const int64_t row = m0 + p * R + rl;
-      const int col = n0 + c8;
-      const float4 lo = *reinterpret_cast<const float4*>(&tile[rl * RS + c8]);
-      const float4 hi = *reinterpret_cast<const float4*>(&tile[rl * RS + c8 + 4]);
-      const float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      float xin[8];
-      {
-        const uint4 pr = pre[p * ITEMS + it];
-        const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+    for (int u = 0; u < 4; ++u) {
+      xin[2 * u] = bf16_to_f32((uint16_t)(pw[u] & 0xFFFFu));
+      xin[2 * u + 1] = bf16_to_f32((uint16_t)(pw[u] >> 16));
+    }
+  };
+  // The full-tile path is one straight line of passes (no join with the
+  // edge path, whose loads would make every pass wait for earlier stores).
+  if constexpr (EPI == EPI_SCALAR) {
+    if (full) {
+      // Addresses: a wave-uniform row base per pass plus a 32-bit element
+      // offset per item (the pass is R rows of N elements).
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          xin[2 * u] = bf16_to_f32((uint16_t)(pw[u] & 0xFFFFu));
-          xin[2 * u + 1] = bf16_to_f32((uint16_t)(pw[u] >> 16));
-        }
-      }
-      if constexpr (EPI == EPI_SCALAR) {
-        if (row >= M) continue;
-        if (pre_ok || (ep.resid == nullptr && col + 8 <= N && (N & 7) == 0)) {
-          if (col >= N) continue;
+      for (int p = 0; p < NP; ++p) {
+        stage(p);
+        uint16_t* obase = ep.out + (m0 + p * R) * (int64_t)N + n0;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          const int idx = tid + it * kThreads;
+          const uint32_t off = (uint32_t)((idx / CPR) * N + (idx % CPR) * 8);
+          float y[8], xin[8];
+          item_y(p, it, y, xin);
           uint32_t ow[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            ow[u] = (uint32_t)f32_to_bf16(xin[2 * u] + ep.g * y[2 * u]) |
-                    ((uint32_t)f32_to_bf16(xin[2 * u + 1] + ep.g * y[2 * u + 1]) << 16);
-          *reinterpret_cast<uint4*>(ep.out + row * N + col) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-        } else {
+            ow[u] = pack_bf16x2(xin[2 * u] + ep.g * y[2 * u], xin[2 * u + 1] + ep.g * y[2 * u + 1]);
+          *reinterpret_cast<uint4*>(obase + off) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        stage(p);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          const int idx = tid + it * kThreads;
+          const int64_t row = m0 + p * R + idx / CPR;
+          const int col = n0 + (idx % CPR) * 8;
+          float y[8], xin[8];
+          item_y(p, it, y, xin);
+          if (row >= M) continue;
           for (int u = 0; u < 8 && col + u < N; ++u) {
             const int64_t o = row * N + col + u;
             const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
-            ep.out[o] = f32_to_bf16(x + ep.g * y[u]);
+            ep.out[o] = (uint16_t)pack_bf16x2(x + ep.g * y[u], 0.f);
           }
         }
-      } else {
-        // Engram pass 1: the block's 256 columns are one partial-sum column
-        // block of one segment (BN = 256 divides d); the 32 consecutive lanes
-        // of a row hold it.
+      }
+    }
+  } else {
+    // Engram pass 1: the block's 256 columns are one partial-sum column block
+    // of one segment (BN = 256 divides d); the 32 consecutive lanes of a row
+    // hold it. Edge tiles (rows past M) read h per item.
+    const int seg = n0 / ep.d;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      stage(p);
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int idx = tid + it * kThreads;
+        const int c8 = (idx % CPR) * 8;
+        const int64_t row = m0 + p * R + idx / CPR;
+        const int c = n0 + c8 - seg * ep.d;
         const bool live = row < M;
-        const int seg = col / ep.d;
-        const int c = col - seg * ep.d;
+        float y[8], xin[8];
+        item_y(p, it, y, xin);
+        if (!full && seg > 0 && live) {
+          const uint4 pr = *reinterpret_cast<const uint4*>(pre_src + row * pre_ld + pre_c0 + c8);
+          const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            xin[2 * u] = bf16_to_f32((uint16_t)(pw[u] & 0xFFFFu));
+            xin[2 * u + 1] = bf16_to_f32((uint16_t)(pw[u] >> 16));
+          }
+        }
         float s0 = 0.f, s1 = 0.f, s2 = 0.f;
         if (seg == 0) {
           uint32_t vw[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            vw[u] = (uint32_t)f32_to_bf16(y[2 * u]) | ((uint32_t)f32_to_bf16(y[2 * u + 1]) << 16);
+          for (int u = 0; u < 4; ++u) vw[u] = pack_bf16x2(y[2 * u], y[2 * u + 1]);
           if (live)
             *reinterpret_cast<uint4*>(ep.v + row * ep.d + c) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
 #pragma unroll
@@ -403,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_pipe_kernel(
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             s0 += y[u] * y[u];
-            s1 += ep.gamma_h[c + u] * ep.gamma_k[c + u] * xin[u] * y[u];
+            s1 += gg[u] * xin[u] * y[u];
             s2 += xin[u] * xin[u];
           }
         }
@@ -576,12 +697,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
   }
 }
 
-template <int BM, int BN, int EPI>
+// BM x BN tiles, K stages of BK through a ring of S, MINB blocks per CU.
+template <int BM, int BN, int BK, int S, int MINB, int EPI>
 hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
                        const EpiArgs& ep, hipStream_t s) {
-  constexpr int BK = PIPE_BK, S = PIPE_STAGES;
+  static_assert(PipeCfg<BM, BN, BK, S>::kLdsBytes * MINB <= 160 * 1024, "LDS per CU");
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
                      static_cast<const uint16_t*>(W), M, N, K, ep);
   return hipGetLastError();
@@ -603,15 +725,26 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
   ep.g = g;
   ep.resid = static_cast<const uint16_t*>(resid);
   ep.out = static_cast<uint16_t*>(out);
-  if (E % PIPE_BK == 0) {
+  if (E % kPipeBK == 0) {
+#if GEMM_CFG == 1
+    // 128-row tiles, two blocks per CU
+    if (d % 256 != 0 && d % 192 == 0)
+      return launch_pipe<128, 192, 32, 4, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+    return launch_pipe<128, 256, 32, 3, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+#elif GEMM_CFG == 2
+    if (d % 256 != 0 && d % 192 == 0)
+      return launch_pipe<128, 192, 64, 2, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+    return launch_pipe<128, 256, 32, 3, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+#else
     // Pick the N tile by rounds of 256 concurrent blocks times block work.
     auto cost = [&](int64_t bn) {
       const int64_t blocks = ((N + 255) / 256) * ((d + bn - 1) / bn);
       return ((blocks + 255) / 256) * bn;
     };
     if (cost(192) < cost(256))
-      return launch_pipe<256, 192, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-    return launch_pipe<256, 256, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+      return launch_pipe<256, 192, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+    return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+#endif
   }
   constexpr int BM = 128, BN = 128;
   const int64_t blocks = ((N + BM - 1) / BM) * ((d + BN - 1) / BN);
@@ -635,7 +768,12 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
-  return launch_pipe<256, 256, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
+#if GEMM_CFG == 1 || GEMM_CFG == 2
+  return launch_pipe<128, 256, 32, 3, 2, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
+#else
+  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d),
+                                                                   (int)E, W, ep, s);
+#endif
 }
 
 }  // namespace pg
