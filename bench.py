@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (for counter scaling)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic.json from two rocprofv3 --pmc counter "
+                        "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run")
     return p.parse_args()
 
 
@@ -96,6 +99,55 @@ def traffic_for(stage, workload):
     if not ent or ent.get("source_digest") != source_digest(KERNEL_SOURCES[stage]):
         return None
     return ent.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_bf16_pipe_kernel",
+                   "copy": "copyBuffer"}
+
+
+def counter_means(path, counter):
+    """Mean per-dispatch value (KiB) of one counter for each kernel family."""
+    import csv
+    sums = {}
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter:
+            continue
+        for fam, key in TRAFFIC_KERNELS.items():
+            if key in row["Kernel_Name"]:
+                d = sums.setdefault(fam, {})
+                d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    # the copy family: only the 1 GiB probe copies (bench.py's other copies are
+    # at most a third of that; FETCH_SIZE reads half of a copy's bytes)
+    if "copy" in sums:
+        sums["copy"] = {k: v for k, v in sums["copy"].items() if v * 1024 > 0.45 * COPY_BYTES}
+    return {fam: sum(d.values()) / len(d) for fam, d in sums.items() if d}
+
+
+def write_traffic(workload, fetch_csv, write_csv):
+    """HBM bytes per launch of the gather and projection kernels: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
+    1 GiB device copy read and write exactly 1 GiB."""
+    fetch = counter_means(fetch_csv, "FETCH_SIZE")
+    write = counter_means(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024)
+    w_scale = COPY_BYTES / (write["copy"] * 1024)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    ent = {}
+    for stage in ("gather", "projection"):
+        rd = fetch[stage] * 1024 * f_scale
+        wr = write[stage] * 1024 * w_scale
+        ent[stage] = {"kernel": TRAFFIC_KERNELS[stage],
+                      "source_digest": source_digest(KERNEL_SOURCES[stage]),
+                      "fetch_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                      "fetch_kib_raw": fetch[stage], "write_kib_raw": write[stage]}
+    ent["copy_scale"] = {"fetch": f_scale, "write": w_scale,
+                         "copy_fetch_kib_raw": fetch["copy"], "copy_write_kib_raw": write["copy"]}
+    rec[workload] = ent
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: ent}, indent=1))
 
 
 def cpu_baseline(wl, n_tok):
@@ -164,6 +216,9 @@ def cpu_baseline(wl, n_tok):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence with no exchange between GPUs)",

@@ -1,35 +1,42 @@
 // Projection GEMMs (gfx950).
 //
 // Y[M x N] = E[M x K] . W[N x K]^T with bf16 inputs and fp32 accumulation on
-// MFMA (v_mfma_f32_16x16x32_bf16). Both operands are K-contiguous, the layout
-// the MFMA A and B fragments take directly.
+// the matrix cores. Both operands are K-contiguous, the layout the MFMA A and
+// B fragments take directly.
 //
-// Main kernel (K a multiple of 32): 256 threads = 4 waves in a 2 x 2 grid,
-// block tile BM x BN (256 x 192 or 256 x 256), wave tile (BM/2) x (BN/2).
-// K advances BK = 64 at a time through LDS rings filled by direct
-// global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes, a
-// wave writes 1 KiB of LDS per instruction), so three K tiles are in flight
-// while one is multiplied and no VGPRs are spent on staging. Each stage
-// buffer is its own LDS object and the loop is unrolled by the ring length so
-// the compiler can tell the buffers apart; the ring is synchronised with
-// counted vmcnt waits and a bare barrier (a __syncthreads() would drain every
-// outstanding load). Within a 64-byte LDS row the four 16-byte K chunks are
-// XOR-swizzled by (row >> 1) & 3, so the 16 rows a fragment read touches fall
-// in distinct banks. Rows past M or N are clamped in-bounds for the loads and
-// never stored.
+// Main kernel (K a multiple of 64): 256 threads = 4 waves in a 2 x 2 grid,
+// block tile BM x BN (256 x 192 or 256 x 256), wave tile (BM/2) x (BN/2)
+// made of 32 x 32 blocks of v_mfma_f32_32x32x16_bf16 (on gfx950 this form
+// sustains far more of the bf16 peak than 16 x 16 x 32). K advances 64 at a
+// time through two-buffer LDS rings for the E and W tiles, filled by direct
+// global->LDS loads (global_load_lds_dwordx4: a lane moves 16 bytes, a wave
+// writes 1 KiB of LDS per instruction; the address is an SGPR base plus a
+// per-lane offset), so no VGPRs are spent on staging. A stage's four K steps
+// interleave: the LDS fragment reads of step s+1 go out between the MFMAs of
+// step s, and the next stage's loads are spread over the steps. The ring is
+// synchronised with counted vmcnt waits and a bare barrier (a
+// __syncthreads() would drain every outstanding load). The four 16-byte K
+// chunks of a row are XOR-swizzled by the row's low bits so a fragment read
+// is free of bank conflicts. Rows past M or N are clamped in-bounds for the
+// loads and never stored.
 //
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
-// 8 XCDs) runs a contiguous range of M-major tiles: the N tiles of one E tile
-// run together on one XCD and share that E tile and W through its L2.
+// 8 XCDs) runs a contiguous range of tiles, walked in groups of 8 M tiles
+// N-major: concurrently running tiles share their E and W panels in one L2.
+//
+// Epilogue: the accumulators are staged through LDS a pass of rows at a
+// time and leave as 16-byte row stores; passes synchronise on LDS only (the
+// stores are never waited for), the bf16 input tile (residual x, or h) is
+// fetched once before the first store, and bf16 packing is one
+// v_cvt_pk_bf16_f32 per pair. Two epilogues: the scalar gate (PageGram §3.1:
+// out = x + g W_V e) and pass 1 of the Engram fusion (Engram notes §3.3-3.4):
+// v = W_V e is stored in bf16 and, per token and 256-column block, the
+// partial sums RMSNorm and the context gate need (sum v^2; per branch sum
+// k^2, sum gamma_h gamma_k h k, sum h^2) go to the workspace, so k is never
+// stored.
 //
 // Fallback kernel (K a multiple of 8): 128 x 128 tile, BK = 64, register-
 // staged double buffer; scalar gate only.
-//
-// Epilogues: the scalar gate (PageGram §3.1: out = x + g W_V e) and pass 1 of
-// the Engram fusion (Engram notes §3.3-3.4): v = W_V e is stored in bf16 and,
-// per token and 128-column block, the partial sums RMSNorm and the context
-// gate need (sum v^2; per branch sum k^2, sum gamma_h gamma_k h k, sum h^2)
-// go to the workspace, so k is never stored.
 //
 // fp32: a plain LDS-tiled FMA GEMM for fp32 tables (tiny workloads).
 #include "common.h"
@@ -47,9 +54,6 @@ constexpr int kThreads = 256;
 constexpr int kColBlock = 256;   // Engram partial-sum column block
 constexpr int kPipeBK = 64;      // K stage of the pipelined kernel
 constexpr int kPipeStages = 2;   // its LDS ring
-#ifndef GEMM_CFG
-#define GEMM_CFG 0
-#endif
 
 enum { EPI_SCALAR = 0, EPI_ENGRAM = 1 };
 
@@ -726,16 +730,6 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
   ep.resid = static_cast<const uint16_t*>(resid);
   ep.out = static_cast<uint16_t*>(out);
   if (E % kPipeBK == 0) {
-#if GEMM_CFG == 1
-    // 128-row tiles, two blocks per CU
-    if (d % 256 != 0 && d % 192 == 0)
-      return launch_pipe<128, 192, 32, 4, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-    return launch_pipe<128, 256, 32, 3, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-#elif GEMM_CFG == 2
-    if (d % 256 != 0 && d % 192 == 0)
-      return launch_pipe<128, 192, 64, 2, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-    return launch_pipe<128, 256, 32, 3, 2, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-#else
     // Pick the N tile by rounds of 256 concurrent blocks times block work.
     auto cost = [&](int64_t bn) {
       const int64_t blocks = ((N + 255) / 256) * ((d + bn - 1) / bn);
@@ -744,7 +738,6 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
     if (cost(192) < cost(256))
       return launch_pipe<256, 192, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
     return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-#endif
   }
   constexpr int BM = 128, BN = 128;
   const int64_t blocks = ((N + BM - 1) / BM) * ((d + BN - 1) / BN);
@@ -754,7 +747,7 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
   return hipGetLastError();
 }
 
-// Engram pass 1 (E % 32 == 0 and d % 256 == 0, checked by the caller).
+// Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller).
 hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
                                int64_t d, int64_t Mbr, const void* h,
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
@@ -768,12 +761,8 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
-#if GEMM_CFG == 1 || GEMM_CFG == 2
-  return launch_pipe<128, 256, 32, 3, 2, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
-#else
   return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d),
                                                                    (int)E, W, ep, s);
-#endif
 }
 
 }  // namespace pg
