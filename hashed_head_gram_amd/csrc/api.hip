@@ -46,6 +46,7 @@ int prepare_layout(const pg_layout* in, DevLayout* L) {
     if (in->S < 1) return PG_EINVAL;
     L->S = (uint64_t)in->S;
     L->S_magic = UINT64_MAX / L->S;
+    L->S_pow2 = (L->S & (L->S - 1)) == 0;
     const int64_t per_page = (int64_t)in->K * in->S;
     for (int i = 0; i < L->O; ++i) {
       const int64_t P = in->pages[i];
@@ -59,6 +60,7 @@ int prepare_layout(const pg_layout* in, DevLayout* L) {
   } else {
     L->S = 1;
     L->S_magic = UINT64_MAX;
+    L->S_pow2 = 1;
     for (int i = 0; i < L->O; ++i)
       for (int k = 0; k < L->K; ++k) {
         const int64_t P = in->head_rows[i][k];

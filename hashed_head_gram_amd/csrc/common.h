@@ -31,6 +31,8 @@ struct DevLayout {
   uint64_t seed;
   uint64_t pad_id;
   uint64_t S, S_magic;
+  int32_t S_pow2;     // S is a power of two: u mod S = u & (S - 1)
+  int32_t pad1;
   int64_t n_rows;
   uint64_t P[kMaxOrders], P_magic[kMaxOrders];
   int64_t base[kMaxOrders];
@@ -90,29 +92,30 @@ __device__ inline void load_role_consts(const DevLayout& L, uint64_t* rc) {
   __syncthreads();
 }
 
+// Canonical IDs are below 2^32, so each product is a 64 x 32-bit multiply.
 __device__ __forceinline__ uint64_t role_hash(const uint64_t* rc, int q,
-                                              const uint64_t* g, int n) {
+                                              const uint32_t* g, int n) {
   const uint64_t* c = rc + q * kRoleStride;
   uint64_t x = c[0];
-  for (int j = 0; j < n; ++j) x ^= g[j] * c[1 + j];
+  for (int j = 0; j < n; ++j) x ^= (uint64_t)g[j] * c[1 + j];
   return mix64(x);
 }
 
 // Canonical ID of token position t of a sequence starting at `seq`
 // (pad_id when t < 0 or the token is outside [0, V)).
-__device__ __forceinline__ uint64_t canon_at(const int32_t* __restrict__ seq,
+__device__ __forceinline__ uint32_t canon_at(const int32_t* __restrict__ seq,
                                              int64_t t, const int32_t* __restrict__ cmap,
                                              int64_t V, uint64_t pad) {
-  if (t < 0) return pad;
+  if (t < 0) return (uint32_t)pad;
   const int32_t tok = seq[t];
-  if (tok < 0 || (int64_t)tok >= V) return pad;
-  return (uint64_t)(uint32_t)cmap[tok];
+  if (tok < 0 || (int64_t)tok >= V) return (uint32_t)pad;
+  return (uint32_t)cmap[tok];
 }
 
 // Row of head k of order i for n-gram g (n = n_min + i), and the page for
 // PageGram (-1 otherwise). rc holds the role constants.
 __device__ __forceinline__ int64_t head_row(const DevLayout& L, const uint64_t* rc,
-                                            const uint64_t* g, int i, int k,
+                                            const uint32_t* g, int i, int k,
                                             uint64_t* b_out, uint64_t* u_out,
                                             int64_t* page_out) {
   const int n = L.n_min + i;
@@ -122,7 +125,7 @@ __device__ __forceinline__ int64_t head_row(const DevLayout& L, const uint64_t* 
   if (L.kind == PG_PAGEGRAM) {
     const uint64_t b = role_hash(rc, i * R, g, n);
     const uint64_t p = mod_magic(b, L.P[i], L.P_magic[i]);
-    const uint64_t slot = mod_magic(u, L.S, L.S_magic);
+    const uint64_t slot = L.S_pow2 ? (u & (L.S - 1)) : mod_magic(u, L.S, L.S_magic);
     *b_out = b;
     *page_out = (int64_t)p;
     return L.base[i] + (int64_t)((p * (uint64_t)L.K + (uint64_t)k) * L.S + slot);
@@ -134,7 +137,7 @@ __device__ __forceinline__ int64_t head_row(const DevLayout& L, const uint64_t* 
 }
 
 __device__ __forceinline__ uint64_t sign_word(const DevLayout& L, const uint64_t* rc,
-                                              const uint64_t* g, int i, int k, int w) {
+                                              const uint32_t* g, int i, int k, int w) {
   if (!L.use_signs) return 0;
   const int R = 1 + L.K + L.K * L.W;
   return role_hash(rc, i * R + 1 + L.K + k * L.W + w, g, L.n_min + i);

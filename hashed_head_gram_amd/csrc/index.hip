@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void index_kernel(
   const int64_t t = tok - b * T;
   const int32_t* seq = tokens + b * T;
   const int n = L.n_min + i;
-  uint64_t g[kMaxOrders];
+  uint32_t g[kMaxOrders];
 #pragma unroll
   for (int j = 0; j < kMaxOrders; ++j)
     g[j] = j < n ? canon_at(seq, t - j, cmap, V, L.pad_id) : 0;
@@ -197,13 +197,37 @@ __global__ __launch_bounds__(kThreads) void index_gather_kernel(
   __shared__ uint64_t rc[kMaxRoles * kRoleStride];
   __shared__ int64_t rowsL[kThreads];
   __shared__ uint64_t signsL[kThreads * kMaxSignWords];
+  __shared__ uint32_t canonL[kThreads + kMaxOrders];
   __shared__ float cb[16];
-  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
-  load_role_consts(L, rc);
   const int OK = L.O * L.K;
   const int64_t N = B * T;
   const int64_t tok0 = (int64_t)blockIdx.x * TB;
   const int tid = threadIdx.x;
+  // Canonical IDs of the block's tokens and the H = n_max - 1 before them,
+  // loaded once per block into LDS: the token loads go out first so their
+  // latency overlaps the derivation of the role constants.
+  const int H = L.n_min + L.O - 2;
+  const int nh = TB + H;
+  int32_t tk[2];
+  bool have[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + q * kThreads;
+    const int64_t gt = tok0 - H + e;
+    have[q] = e < nh && gt >= 0 && gt < N;
+    tk[q] = have[q] ? tokens[gt] : 0;
+  }
+  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
+  load_role_consts(L, rc);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + q * kThreads;
+    if (e >= nh) continue;
+    const bool ok = have[q] && tk[q] >= 0 && (int64_t)tk[q] < V;
+    canonL[e] = ok ? (uint32_t)cmap[tk[q]] : (uint32_t)L.pad_id;
+    if (status && have[q] && e >= H && !ok) atomicOr(status, 1);
+  }
+  __syncthreads();
   if (tid < TB * OK) {
     const int tl = tid / OK;
     const int rem = tid - tl * OK;
@@ -211,18 +235,12 @@ __global__ __launch_bounds__(kThreads) void index_gather_kernel(
     const int k = rem - i * L.K;
     const int64_t tok = tok0 + tl;
     if (tok < N) {
-      const int64_t b = tok / T;
-      const int64_t t = tok - b * T;
-      const int32_t* seq = tokens + b * T;
+      const int64_t t = tok % T;
       const int n = L.n_min + i;
-      uint64_t g[kMaxOrders];
+      uint32_t g[kMaxOrders];
 #pragma unroll
       for (int j = 0; j < kMaxOrders; ++j)
-        g[j] = j < n ? canon_at(seq, t - j, cmap, V, L.pad_id) : 0;
-      if (status && i == 0 && k == 0) {
-        const int32_t tk = seq[t];
-        if (tk < 0 || (int64_t)tk >= V) atomicOr(status, 1);
-      }
+        g[j] = j < n ? (t - j >= 0 ? canonL[H + tl - j] : (uint32_t)L.pad_id) : 0u;
       uint64_t bh, u;
       int64_t page;
       rowsL[tid] = head_row(L, rc, g, i, k, &bh, &u, &page);
