@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (for counter scaling)")
+    p.add_argument("--page-cache", action="store_true",
+                   help="flash page-cache figures (reads/token under an LRU RAM cache) "
+                        "of the 20B NF4 table in the PageGram S=4, S=15 and Engram-style "
+                        "layouts, from pg_index rows of the token pool")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 --pmc counter "
                         "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run")
@@ -150,6 +154,57 @@ def write_traffic(workload, fetch_csv, write_csv):
     print(json.dumps({workload: ent}, indent=1))
 
 
+PAGE_CACHE_LAYOUTS = ["pagegram20b_nf4_16x4096", "pagegram20b_nf4_s15_16x4096",
+                      "engram20b_nf4_16x4096"]
+PAGE_CACHE_MIB = [0, 16, 64, 256, 1024, 4096]
+
+
+def page_cache(batches):
+    """Reads/token of the 20B NF4 table under an LRU RAM page cache of 4 KiB
+    blocks, for the three layouts, over `batches` batches of the token stream.
+    Rows come from pg_index on the GPU; blocks and the LRU run on the host."""
+    import numpy as np
+    import torch
+
+    import hashed_head_gram_amd as pg
+    import synth
+    from synth import configs
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for name in PAGE_CACHE_LAYOUTS:
+        wl = configs.workload(name)
+        lay_d = wl["layout"]
+        layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
+                                pages=lay_d["pages"], head_rows=lay_d["head_rows"],
+                                hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
+                                n_min=lay_d["n_min"], n_max=lay_d["n_max"],
+                                pad_id=wl["canon_vocab"])
+        O = lay_d["n_max"] - lay_d["n_min"] + 1
+        K, W = lay_d["K"], (lay_d["r"] + 63) // 64
+        cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
+        blocks = []
+        t0 = time.perf_counter()
+        for j in range(batches):
+            toks = torch.from_numpy(synth.tokens(wl, batch=j)).to(dev)
+            N = toks.numel()
+            rows = torch.empty(N, O, K, dtype=torch.int64, device=dev)
+            signs = torch.empty(N, O, K, W, dtype=torch.int64, device=dev)
+            pg.pg_index(layout, toks, cmap, rows, signs)
+            blocks.append(pg.pg_flash_blocks(layout, pg.PG_NF4, rows.cpu().numpy()))
+        blocks = np.concatenate([b.reshape(b.shape[0], -1) for b in blocks])
+        t1 = time.perf_counter()
+        per = {}
+        for mib in PAGE_CACHE_MIB:
+            st = pg.pg_lru_cache_sim(blocks, mib * 1024 * 1024 // 4096)
+            per[f"{mib}MiB"] = st["misses"] / st["tokens"]
+        t2 = time.perf_counter()
+        res[name] = {"reads_per_token": per, "tokens": int(blocks.shape[0]),
+                     "uncached_reads_per_token": st["distinct"] / st["tokens"],
+                     "index_s": t1 - t0, "lru_s": (t2 - t1) / len(PAGE_CACHE_MIB)}
+    return res
+
+
 def cpu_baseline(wl, n_tok):
     """The CPU oracle on the first n_tok tokens of the workload's stream."""
     import numpy as np
@@ -218,6 +273,16 @@ def main():
     args = parse()
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
+        return
+    if args.page_cache:
+        line = {"metric": "flash reads per token under an LRU RAM page cache (4 KiB blocks)",
+                "unit": "reads/token", "higher_is_better": False, "n_gpus": 1,
+                "data": "synthetic (seeded Zipf token stream of the 20B workloads, "
+                        f"{args.steps} batches of 16 x 4096 tokens)",
+                "config": {"workload": "20B NF4 table, three layouts",
+                           "cache_MiB": PAGE_CACHE_MIB},
+                "layouts": page_cache(args.steps)}
+        print(json.dumps(line), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -42,6 +42,10 @@ class PgFuse(ctypes.Structure):
                 ("conv_dil", _i32), ("increment_only", _i32), ("reserved", _i32)]
 
 
+class PgCacheStats(ctypes.Structure):
+    _fields_ = [("tokens", _i64), ("lookups", _i64), ("distinct", _i64), ("misses", _i64)]
+
+
 _P = ctypes.POINTER
 _SIGS = {
     "pg_index": (_i32, [_P(PgLayout), _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp,
@@ -57,6 +61,8 @@ _SIGS = {
     "pg_hash_version": (ctypes.c_uint32, []),
     "pg_layout_rows": (_i32, [_P(PgLayout), _P(_i64)]),
     "pg_workspace_size": (_i64, [_P(PgLayout), _P(PgFuse), _i64, _i64]),
+    "pg_flash_blocks": (_i32, [_P(PgLayout), _i32, _vp, _i64, _vp]),
+    "pg_lru_cache_sim": (_i32, [_vp, _i64, _i32, _i64, _P(PgCacheStats)]),
 }
 
 _lib = None
@@ -211,3 +217,31 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# Flash page-cache simulation (host arrays)
+
+
+def pg_flash_blocks(layout, table_dtype, rows):
+    """4 KiB block of each row; rows: host int64 numpy array of any shape."""
+    import numpy as np
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty_like(rows)
+    _check("pg_flash_blocks", lib().pg_flash_blocks(
+        ctypes.byref(layout), int(table_dtype), rows.ctypes.data, rows.size,
+        out.ctypes.data))
+    return out
+
+
+def pg_lru_cache_sim(blocks, capacity_blocks):
+    """LRU run over blocks [n_tok, per_token] (host int64); returns the counters."""
+    import numpy as np
+    blocks = np.ascontiguousarray(blocks, dtype=np.int64)
+    n_tok = blocks.shape[0]
+    per = int(blocks.size // n_tok) if n_tok else 1
+    st = PgCacheStats()
+    _check("pg_lru_cache_sim", lib().pg_lru_cache_sim(
+        blocks.ctypes.data, n_tok, per, int(capacity_blocks), ctypes.byref(st)))
+    return dict(tokens=st.tokens, lookups=st.lookups, distinct=st.distinct,
+                misses=st.misses)

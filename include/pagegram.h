@@ -261,6 +261,52 @@ PG_API int pg_layout_rows(const pg_layout* layout, int64_t* n_rows);
 PG_API int64_t pg_workspace_size(const pg_layout* layout, const pg_fuse* fuse,
                                  int64_t B, int64_t T);
 
+/* ------------------------------------------------------------------------
+ * Flash page-cache simulation (host code; PageGram tech report §2.3, §3.3,
+ * §8 Fig. 4a and appendix D). A table kept on flash is read in 4 KiB blocks;
+ * a RAM page cache with LRU replacement holds whole blocks; each lookup whose
+ * block is not cached is one random flash read.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * pg_flash_blocks -- the 4 KiB block holding each looked-up row, in the
+ * pages' storage order. PageGram: a page is K*S consecutive head rows; when a
+ * page fits in a block, floor(4096 / page_bytes) whole pages share a block
+ * (three 1,088-byte NF4 pages at S = 4, one 4,080-byte page at S = 15),
+ * otherwise a page spans ceil(page_bytes / 4096) blocks and a row lies in
+ * the block of its byte offset. Engram-style: each per-head table starts on
+ * a fresh block and packs floor(4096 / row_bytes) rows per block (120 NF4
+ * rows of 34 bytes).
+ *   table_dtype  PG_F32 / PG_BF16 / PG_NF4 (row bytes 4r / 2r / r/2 + 2)
+ *   rows         host int64 [n] row indices (e.g. pg_index's rows, copied
+ *                to the host); blocks_out host int64 [n].
+ * Errors: PG_EINVAL for a bad layout, dtype or NULL pointer with n > 0;
+ * PG_ERANGE for a row outside [0, R). Thread-safe, allocates nothing.
+ */
+PG_API int pg_flash_blocks(const pg_layout* layout, int32_t table_dtype,
+                           const int64_t* rows, int64_t n, int64_t* blocks_out);
+
+/* Counters of one LRU run. */
+typedef struct {
+  int64_t tokens;     /* tokens offered */
+  int64_t lookups;    /* row lookups (tokens * per_token) */
+  int64_t distinct;   /* sum over tokens of distinct blocks (uncached reads) */
+  int64_t misses;     /* flash reads with the cache */
+} pg_cache_stats;
+
+/*
+ * pg_lru_cache_sim -- offers each token's distinct blocks (first-use order,
+ * duplicates within the token dropped) to an LRU cache of capacity_blocks
+ * 4 KiB blocks (0 = no cache) and counts the misses.
+ *   blocks  host int64 [n_tok][per_token] (pg_flash_blocks of [n_tok][O][K]
+ *           rows; per_token = O * K)
+ * Errors: PG_EINVAL for NULL pointers with n_tok > 0, per_token < 1 or a
+ * negative capacity. Allocates host memory for the cache state only for the
+ * duration of the call; thread-safe.
+ */
+PG_API int pg_lru_cache_sim(const int64_t* blocks, int64_t n_tok, int32_t per_token,
+                            int64_t capacity_blocks, pg_cache_stats* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,13 @@ ENGRAM_27B_PRIMES = [
     4453223, 4453231, 4453259, 4453271, 4453291, 4453321, 4453331, 4453349,
 ]
 
+# Engram-style comparison layout for the 20B NF4 table: the first 16 primes
+# >= 312,500,000 / 16 (the page-cache comparison of PageGram §8 at equal size).
+ENGRAM_20B_PRIMES = [
+    19531261, 19531289, 19531327, 19531339, 19531381, 19531387, 19531403, 19531409,
+    19531423, 19531433, 19531441, 19531493, 19531517, 19531541, 19531543, 19531553,
+]
+
 # Stream identifiers of the counter-based value generator (synth.gen).
 STREAM_TABLE = 1
 STREAM_NF4_SCALE = 2
@@ -100,6 +107,28 @@ WORKLOADS = {
         act_dtype="bf16", d=2560, w_sigma=0.05, resid_sigma=1.0,
         gate="engram", M=4, eps=1e-6, conv_k=4, conv_dil=3,
         conv_sigma=0.5, gamma="ones", data_seed=5,
+    ),
+    # The 20B NF4 table at S = 15: a page of K*S = 120 NF4 head rows is
+    # 120 * 34 = 4080 bytes, one 4 KiB block (PageGram §3.3); P_n chosen so the
+    # table keeps the 20B workload's 156.25M rows per order (1,302,083 pages).
+    "pagegram20b_nf4_s15_16x4096": dict(
+        layout=_layout("pagegram", K=8, S=15, r=64,
+                       pages=[1302083, 1302083]),
+        vocab=128000, canon_vocab=98000, canon="surjective", map_seed=4,
+        B=16, T=4096, token_dist="zipf", zipf_s=1.1, token_seed=4,
+        table_dtype="nf4", table_sigma=0.02, table_seed=6,
+        act_dtype="bf16", d=2560, w_sigma=0.05, resid_sigma=1.0,
+        gate="scalar", g=0.5, data_seed=4,
+    ),
+    # The same 20B NF4 table in the Engram-style layout (16 prime head tables,
+    # 312,502,740 rows): the comparison side of the flash page-cache figures.
+    "engram20b_nf4_16x4096": dict(
+        layout=_layout("engram", K=8, S=1, r=64, primes=ENGRAM_20B_PRIMES),
+        vocab=128000, canon_vocab=98000, canon="surjective", map_seed=4,
+        B=16, T=4096, token_dist="zipf", zipf_s=1.1, token_seed=4,
+        table_dtype="nf4", table_sigma=0.02, table_seed=7,
+        act_dtype="bf16", d=2560, w_sigma=0.05, resid_sigma=1.0,
+        gate="scalar", g=0.5, data_seed=4,
     ),
 }
 

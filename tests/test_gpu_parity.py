@@ -77,7 +77,7 @@ def e_as_np(c, e):
     return e.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(len(configs.ORDER)))
 def test_index_bit_exact(i):
     c = case(i)
     got = c.run_index()
@@ -91,7 +91,7 @@ def test_index_bit_exact(i):
     assert got["status"].item() == 0
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(len(configs.ORDER)))
 def test_gather_bit_exact(i):
     c = case(i)
     e = c.run_index_gather()
@@ -109,7 +109,7 @@ def test_gather_bit_exact(i):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(len(configs.ORDER)))
 def test_forward_within_tolerance(i):
     c = case(i)
     out = c.run_forward()
@@ -137,7 +137,7 @@ def test_forward_within_tolerance(i):
     assert err < tol and err_inc < tol
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(len(configs.ORDER)))
 def test_forward_equals_stage_composition(i):
     # pg_forward == pg_index_gather -> pg_project_gate == pg_index -> pg_gather
     # -> pg_project_gate, bit for bit (same products, same summation order).

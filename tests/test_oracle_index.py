@@ -315,7 +315,8 @@ def test_prime_sizes_and_parameter_parity():
             i += 1
         return True
     for plist, start in ((configs.ENGRAM_200M_PRIMES, 195313),
-                         (configs.ENGRAM_27B_PRIMES, 4453125)):
+                         (configs.ENGRAM_27B_PRIMES, 4453125),
+                         (configs.ENGRAM_20B_PRIMES, 312_500_000 // 16)):
         assert len(set(plist)) == 16 and all(isprime(p) for p in plist)
         assert plist == sorted(plist) and plist[0] >= start
         # the first 16 primes >= start: no prime is skipped
@@ -334,10 +335,21 @@ def test_prime_sizes_and_parameter_parity():
     # 20B NF4 table: 312.5M rows of 64.
     r4 = oracle.layout_bases(configs.workload(3)["layout"])[1]
     assert abs(r4 * 64 - 20e9) / 20e9 < 1e-6
+    # The same table at S = 15 (PageGram §3.3): a page is K*S = 120 NF4 head
+    # rows = 120 * 34 = 4080 bytes inside one 4096-byte block, and the row
+    # count stays within 1e-6 of 20B parameters.
+    # the Engram-style comparison layout of the same 20B table
+    r_en = oracle.layout_bases(configs.workload("engram20b_nf4_16x4096")["layout"])[1]
+    assert abs(r_en * 64 - 20e9) / 20e9 < 1e-4
+    lay15 = configs.workload(5)["layout"]
+    assert lay15["S"] == 15 and lay15["K"] * lay15["S"] == 120
+    assert lay15["K"] * lay15["S"] * (lay15["r"] // 2 + 2) == 4080 <= 4096
+    r15 = oracle.layout_bases(lay15)[1]
+    assert abs(r15 * 64 - 20e9) / 20e9 < 1e-6
 
 
 def test_canonical_maps():
-    for i in range(5):
+    for i in range(len(configs.ORDER)):
         wl = configs.workload(i)
         m = synth.canon_map(wl)
         assert len(m) == wl["vocab"]
