@@ -61,6 +61,12 @@ _SIGS = {
     "pg_hash_version": (ctypes.c_uint32, []),
     "pg_layout_rows": (_i32, [_P(PgLayout), _P(_i64)]),
     "pg_workspace_size": (_i64, [_P(PgLayout), _P(PgFuse), _i64, _i64]),
+    "pg_backward_workspace_size": (_i64, [_P(PgLayout), _P(PgFuse), _i64, _i64]),
+    "pg_backward_scalar": (_i32, [_P(PgLayout), _P(PgFuse), _vp, _vp, _vp, _vp, _vp, _i64,
+                                  _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "pg_row_rms_step": (_i32, [_P(PgLayout), _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _f32,
+                               _f32, _f32, _f32, _vp]),
+    "pg_row_rms_flush": (_i32, [_P(PgLayout), _vp, _vp, _vp, _i64, _f32, _f32, _f32, _vp]),
     "pg_flash_blocks": (_i32, [_P(PgLayout), _i32, _vp, _i64, _vp]),
     "pg_lru_cache_sim": (_i32, [_vp, _i64, _i32, _i64, _P(PgCacheStats)]),
 }
@@ -217,6 +223,42 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# Backward pass and table update
+
+
+def pg_backward_workspace_size(layout, fuse, B, T):
+    v = lib().pg_backward_workspace_size(ctypes.byref(layout), ctypes.byref(fuse), int(B),
+                                         int(T))
+    if v < 0:
+        raise PagegramError("pg_backward_workspace_size", v)
+    return v
+
+
+def pg_backward_scalar(layout, fuse, rows, signs, e, dy, W, B, T, dW, de, urows, ugrad,
+                       n_unique, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pg_backward_scalar", lib().pg_backward_scalar(
+        ctypes.byref(layout), ctypes.byref(fuse), _ptr(rows), _ptr(signs), _ptr(e), _ptr(dy),
+        _ptr(W), int(B), int(T), _ptr(dW), _ptr(de), _ptr(urows), _ptr(ugrad),
+        _ptr(n_unique), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pg_row_rms_step(layout, urows, ugrad, n_unique, max_unique, table, vhat, last_step, step,
+                    lr, beta2=0.95, weight_decay=0.0, eps=1e-8, stream=None):
+    _check("pg_row_rms_step", lib().pg_row_rms_step(
+        ctypes.byref(layout), _ptr(urows), _ptr(ugrad), _ptr(n_unique), int(max_unique),
+        _ptr(table), _ptr(vhat), _ptr(last_step), int(step), float(lr), float(beta2),
+        float(weight_decay), float(eps), _stream(stream)))
+
+
+def pg_row_rms_flush(layout, table, vhat, last_step, step, lr, beta2=0.95, weight_decay=0.0,
+                     stream=None):
+    _check("pg_row_rms_flush", lib().pg_row_rms_flush(
+        ctypes.byref(layout), _ptr(table), _ptr(vhat), _ptr(last_step), int(step), float(lr),
+        float(beta2), float(weight_decay), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -301,4 +301,91 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
   return run_project(fuse, e, B, T, e_dim, W, resid, out, ws, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass and table update
+
+namespace {
+
+// Shapes the backward pass supports; fills N, d, E, L.
+int check_backward(const pg_layout* layout, const pg_fuse* fuse, int64_t B, int64_t T,
+                   DevLayout* L, int64_t* N, int64_t* E, int64_t* Lk) {
+  int st = prepare_layout(layout, L);
+  if (st != PG_OK) return st;
+  if (!fuse || B < 0 || T < 0) return PG_EINVAL;
+  if (T > 0 && B > kMaxTokens / T) return PG_ERANGE;
+  if (fuse->gate != PG_GATE_SCALAR || fuse->dtype != PG_BF16) return PG_EUNSUPPORTED;
+  if (fuse->d < 64 || fuse->d % 64) return PG_EUNSUPPORTED;
+  *N = B * T;
+  *E = (int64_t)L->O * L->K * L->r;
+  if (*E % 8) return PG_EUNSUPPORTED;
+  *Lk = *N * L->O * L->K;
+  if (*Lk >= ((int64_t)1 << 31) || L->n_rows > (int64_t)UINT32_MAX) return PG_ERANGE;
+  return PG_OK;
+}
+
+}  // namespace
+
+PG_API int64_t pg_backward_workspace_size(const pg_layout* layout, const pg_fuse* fuse,
+                                          int64_t B, int64_t T) {
+  DevLayout L;
+  int64_t N, E, Lk;
+  const int st = check_backward(layout, fuse, B, T, &L, &N, &E, &Lk);
+  if (st != PG_OK) return st;
+  return pg::backward_plan(N, fuse->d, E, Lk).bytes;
+}
+
+PG_API int pg_backward_scalar(const pg_layout* layout, const pg_fuse* fuse, const int64_t* rows,
+                              const uint64_t* signs, const void* e, const void* dy,
+                              const void* W, int64_t B, int64_t T, float* dW, float* de,
+                              int64_t* urows, float* ugrad, int64_t* n_unique, void* workspace,
+                              int64_t workspace_bytes, hipStream_t stream) {
+  DevLayout L;
+  int64_t N, E, Lk;
+  int st = check_backward(layout, fuse, B, T, &L, &N, &E, &Lk);
+  if (st != PG_OK) return st;
+  if (!n_unique) return PG_EINVAL;
+  if (N == 0) return hip_status(pg::launch_set_i64(n_unique, 0, stream));
+  if (!rows || (L.use_signs && !signs) || !e || !dy || !W || !dW || !de || !urows || !ugrad)
+    return PG_EINVAL;
+  if (!aligned(e, 16) || !aligned(dy, 16) || !aligned(W, 16) || !aligned(dW, 16) ||
+      !aligned(de, 16))
+    return PG_EINVAL;
+  const pg::BackwardPlan p = pg::backward_plan(N, fuse->d, E, Lk);
+  if (!workspace || workspace_bytes < p.bytes || !aligned(workspace, 256)) return PG_EINVAL;
+  return hip_status(pg::launch_backward_scalar(L, p, fuse->g, rows, signs, e, dy, W, N, fuse->d,
+                                               dW, de, urows, ugrad, n_unique, workspace,
+                                               stream));
+}
+
+PG_API int pg_row_rms_step(const pg_layout* layout, const int64_t* urows, const float* ugrad,
+                           const int64_t* n_unique, int64_t max_unique, float* table, float* vhat,
+                           int64_t* last_step, int64_t step, float lr, float beta2,
+                           float weight_decay, float eps, hipStream_t stream) {
+  DevLayout L;
+  const int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  if (max_unique < 0 || step < 1 || !(lr >= 0.f) || !(beta2 >= 0.f && beta2 < 1.f) ||
+      !(weight_decay >= 0.f) || !(eps >= 0.f) || lr * weight_decay >= 1.f)
+    return PG_EINVAL;
+  if (max_unique == 0) return PG_OK;
+  if (!urows || !ugrad || !n_unique || !table || !vhat || !last_step) return PG_EINVAL;
+  return hip_status(pg::launch_rms_step(urows, ugrad, n_unique, max_unique, L.r, table, vhat,
+                                        last_step, step, lr, beta2, weight_decay, eps, stream));
+}
+
+PG_API int pg_row_rms_flush(const pg_layout* layout, float* table, float* vhat,
+                            int64_t* last_step, int64_t step, float lr, float beta2,
+                            float weight_decay, hipStream_t stream) {
+  DevLayout L;
+  const int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  if (step < 0 || !(lr >= 0.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(weight_decay >= 0.f) ||
+      lr * weight_decay >= 1.f)
+    return PG_EINVAL;
+  if (L.n_rows == 0) return PG_OK;
+  if (!table || !vhat || !last_step) return PG_EINVAL;
+  return hip_status(pg::launch_rms_flush(L.n_rows, L.r, table, vhat, last_step, step, lr, beta2,
+                                         weight_decay, stream));
+}
+
 }  // extern "C"

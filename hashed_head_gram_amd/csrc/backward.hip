@@ -1,0 +1,463 @@
+// Backward pass of the scalar-gated path and the sparse row-wise table update
+// (gfx950). PageGram tech report §3.3 (row-wise RMS optimiser with replayed
+// decay), §9.1 (beta2 = 0.95) and §9.4 check 4 (sparse gradient == dense).
+//
+//   de = g dy W                 (projection GEMM, fp32 out)
+//   dW = g dy^T e               (split-K GEMM over tokens, fp32 partials,
+//                                reduced in split order)
+//   table gradient: lookups (t, n, k) sorted by row with a stable LSD radix
+//   sort (4-bit digits), then one wave per distinct row sums
+//   s_{t,n,k} (.) de[t][(n,k) slice] over its lookups in sorted order, which
+//   is lookup order (stable sort) -- deterministic, no atomics on values.
+//   step: one wave per distinct row applies the replayed decay of the steps
+//   the row missed and the RMS step of this one.
+#include "common.h"
+
+namespace pg {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRadixBits = 4;
+constexpr int kDigits = 1 << kRadixBits;
+constexpr int kItems = 8;                          // items per thread
+constexpr int kTile = kThreads * kItems;           // items per block
+
+// ---------------------------------------------------------------------------
+// Transpose (bf16): out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad.
+
+__global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
+    const uint16_t* __restrict__ in, int64_t rows, int64_t cols, int64_t ld_in,
+    uint16_t* __restrict__ out, int64_t rows_pad, int64_t ld_out) {
+  __shared__ uint16_t t[64][66];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int rr = ty + 4 * q;
+    const int64_t r = r0 + rr, c = c0 + tx;
+    t[rr][tx] = (r < rows && c < cols) ? in[r * ld_in + c] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int cc = ty + 4 * q;
+    const int64_t c = c0 + cc, r = r0 + tx;
+    if (c < cols && r < rows_pad) out[c * ld_out + r] = t[tx][cc];
+  }
+}
+
+// out[i] = sum_{s < splits} part[s * n + i], summed in s order.
+__global__ __launch_bounds__(kThreads) void reduce_splits_kernel(
+    const float* __restrict__ part, int splits, int64_t n, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * n + i];
+    out[i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable LSD radix sort of (uint32 key, int32 value) pairs, 4-bit digits.
+// Block b owns items [b * kTile, (b+1) * kTile); thread t of it owns the
+// kItems consecutive items starting at b * kTile + t * kItems.
+
+// keys[i] (row as uint32) and vals[i] = i for the lookups.
+__global__ __launch_bounds__(kThreads) void sort_init_kernel(
+    const int64_t* __restrict__ rows, int64_t n, uint32_t* __restrict__ keys,
+    int32_t* __restrict__ vals) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    keys[i] = (uint32_t)rows[i];
+    vals[i] = (int32_t)i;
+  }
+}
+
+// counts[d * nblk + b] = number of block b's keys with digit d.
+__global__ __launch_bounds__(kThreads) void radix_hist_kernel(
+    const uint32_t* __restrict__ keys, int64_t n, int shift, int32_t* __restrict__ counts) {
+  __shared__ int32_t c[kDigits];
+  if (threadIdx.x < kDigits) c[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = base + q;
+    if (i < n) atomicAdd(&c[(keys[i] >> shift) & (kDigits - 1)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < kDigits) counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = c[threadIdx.x];
+}
+
+// In-place exclusive scan of m int32 values by one block; total -> *total.
+__global__ __launch_bounds__(kThreads) void scan_small_kernel(int32_t* __restrict__ a, int64_t m,
+                                                             int32_t* __restrict__ total) {
+  __shared__ int32_t sums[kThreads];
+  const int64_t per = (m + kThreads - 1) / kThreads;
+  const int64_t lo = threadIdx.x * per, hi = lo + per < m ? lo + per : m;
+  int32_t s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += a[i];
+  sums[threadIdx.x] = s;
+  __syncthreads();
+  // exclusive scan of the 256 thread sums (thread 0 walks them: 256 adds)
+  if (threadIdx.x == 0) {
+    int32_t run = 0;
+    for (int t = 0; t < kThreads; ++t) {
+      const int32_t v = sums[t];
+      sums[t] = run;
+      run += v;
+    }
+    if (total) *total = run;
+  }
+  __syncthreads();
+  int32_t run = sums[threadIdx.x];
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+}
+
+// Stable scatter of one digit pass; offs = scanned counts (digit-major).
+__global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
+    const uint32_t* __restrict__ kin, const int32_t* __restrict__ vin, int64_t n, int shift,
+    const int32_t* __restrict__ offs, uint32_t* __restrict__ kout, int32_t* __restrict__ vout) {
+  __shared__ int32_t F[kDigits * kThreads];       // [digit][thread] counts, then prefixes
+  __shared__ int32_t tsum[kThreads];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)t * kItems;
+  uint32_t k[kItems];
+  int32_t v[kItems];
+  int dg[kItems];
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = base + q;
+    const bool live = i < n;
+    k[q] = live ? kin[i] : 0u;
+    v[q] = live ? vin[i] : 0;
+    dg[q] = live ? (int)((k[q] >> shift) & (kDigits - 1)) : -1;
+  }
+#pragma unroll
+  for (int d = 0; d < kDigits; ++d) {
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kItems; ++q) cnt += dg[q] == d;
+    F[d * kThreads + t] = cnt;
+  }
+  __syncthreads();
+  // exclusive scan of F (digit-major, 4096 entries): thread j owns 16
+  // consecutive entries, all of digit j / 16
+  int32_t loc[kDigits];
+  int32_t run = 0;
+#pragma unroll
+  for (int q = 0; q < kDigits; ++q) {
+    loc[q] = run;
+    run += F[t * kDigits + q];
+  }
+  tsum[t] = run;
+  __syncthreads();
+  if (t == 0) {
+    int32_t acc = 0;
+    for (int j = 0; j < kThreads; ++j) {
+      const int32_t x = tsum[j];
+      tsum[j] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kDigits; ++q) F[t * kDigits + q] = loc[q] + tsum[t];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    if (dg[q] < 0) continue;
+    const int d = dg[q];
+    int rank = 0;
+#pragma unroll
+    for (int p = 0; p < q; ++p) rank += dg[p] == d;
+    const int64_t pos = (int64_t)offs[(int64_t)d * gridDim.x + blockIdx.x] +
+                        (F[d * kThreads + t] - F[d * kThreads]) + rank;
+    kout[pos] = k[q];
+    vout[pos] = v[q];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segments of equal keys in the sorted array.
+
+// flags[i] = 1 where a new key starts; per-block sums -> bsum[b].
+__global__ __launch_bounds__(kThreads) void seg_flags_kernel(
+    const uint32_t* __restrict__ keys, int64_t n, int32_t* __restrict__ flags,
+    int32_t* __restrict__ bsum) {
+  __shared__ int32_t s[kThreads];
+  const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+  int32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = base + q;
+    if (i < n) {
+      const int32_t f = (i == 0 || keys[i] != keys[i - 1]) ? 1 : 0;
+      flags[i] = f;
+      c += f;
+    }
+  }
+  s[threadIdx.x] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int j = 0; j < kThreads; ++j) acc += s[j];
+    bsum[blockIdx.x] = acc;
+  }
+}
+
+// Segment id of every head; seg_start[id] = its position; the last block
+// also writes the sentinel seg_start[n_unique] = n and *n_unique.
+__global__ __launch_bounds__(kThreads) void seg_starts_kernel(
+    const int32_t* __restrict__ flags, int64_t n, const int32_t* __restrict__ boff,
+    const int32_t* __restrict__ total, int32_t* __restrict__ seg_start,
+    int64_t* __restrict__ n_unique) {
+  __shared__ int32_t s[kThreads];
+  const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+  int32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = base + q;
+    if (i < n) c += flags[i];
+  }
+  s[threadIdx.x] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int j = 0; j < kThreads; ++j) {
+      const int32_t x = s[j];
+      s[j] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  int32_t id = boff[blockIdx.x] + s[threadIdx.x];
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int64_t i = base + q;
+    if (i < n && flags[i]) seg_start[id++] = (int32_t)i;
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+    seg_start[*total] = (int32_t)n;
+    *n_unique = *total;
+  }
+}
+
+// One wave per distinct row: urows[s], ugrad[s][0..r) = sum over its lookups
+// (sorted order) of sign * de slice.
+__global__ __launch_bounds__(kThreads) void seg_reduce_kernel(
+    const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
+    const int32_t* __restrict__ seg_start, const int64_t* __restrict__ n_unique, int OK, int r,
+    int W, int use_signs, const float* __restrict__ de, const uint64_t* __restrict__ signs,
+    int64_t* __restrict__ urows, float* __restrict__ ugrad) {
+  const int64_t sidx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (sidx >= *n_unique) return;
+  const int32_t i0 = seg_start[sidx], i1 = seg_start[sidx + 1];
+  const int64_t E = (int64_t)OK * r;
+  if (lane == 0) urows[sidx] = (int64_t)keys[i0];
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    const int j = j0 + lane;
+    if (j >= r) break;
+    float acc = 0.f;
+    for (int32_t i = i0; i < i1; ++i) {
+      const int64_t q = vals[i];
+      const int64_t tok = q / OK;
+      const int slot = (int)(q - tok * OK);
+      float x = de[tok * E + (int64_t)slot * r + j];
+      if (use_signs && ((signs[q * W + (j >> 6)] >> (j & 63)) & 1ull)) x = -x;
+      acc += x;
+    }
+    ugrad[sidx * r + j] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise RMS step and flush.
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) x += __shfl_xor(x, sh, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads) void rms_step_kernel(
+    const int64_t* __restrict__ urows, const float* __restrict__ ugrad,
+    const int64_t* __restrict__ n_unique, int r, float* __restrict__ table,
+    float* __restrict__ vhat, int64_t* __restrict__ last, int64_t step, float lr, float beta2,
+    float wd, float eps) {
+  const int64_t sidx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (sidx >= *n_unique) return;
+  const int64_t row = urows[sidx];
+  const float* g = ugrad + sidx * r;
+  float ss = 0.f;
+  for (int j = lane; j < r; j += 64) ss += g[j] * g[j];
+  const float m = wave_sum(ss) / (float)r;
+  int64_t k = step - last[row];
+  if (k < 1) k = 1;
+  const float v = powf(beta2, (float)k) * vhat[row] + (1.0f - beta2) * m;
+  const float decay = powf(1.0f - lr * wd, (float)k);
+  const float inv = lr / (sqrtf(v) + eps);
+  float* th = table + row * r;
+  for (int j = lane; j < r; j += 64) th[j] = th[j] * decay - inv * g[j];
+  if (lane == 0) {
+    vhat[row] = v;
+    last[row] = step;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rms_flush_kernel(
+    int64_t R, int r, float* __restrict__ table, float* __restrict__ vhat,
+    int64_t* __restrict__ last, int64_t step, float lr, float beta2, float wd) {
+  for (int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x; row < R;
+       row += (int64_t)gridDim.x * kThreads) {
+    const int64_t k = step - last[row];
+    if (k <= 0) continue;
+    const float decay = powf(1.0f - lr * wd, (float)k);
+    float* th = table + row * r;
+    for (int j = 0; j < r; ++j) th[j] *= decay;
+    vhat[row] *= powf(beta2, (float)k);
+    last[row] = step;
+  }
+}
+
+__global__ void set_i64_kernel(int64_t* p, int64_t v) { *p = v; }
+
+int64_t al(int64_t x) { return (x + 255) / 256 * 256; }
+
+unsigned grid_for(int64_t n, int64_t per_block) {
+  int64_t b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > 1048576) b = 1048576;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+// Geometry of the backward workspace.
+BackwardPlan backward_plan(int64_t N, int64_t d, int64_t E, int64_t L) {
+  BackwardPlan p{};
+  const int64_t tiles = ((d + 255) / 256) * ((E + 255) / 256);
+  const int64_t kblk = (N + 63) / 64;              // 64-token K stages
+  int64_t splits = (256 + tiles - 1) / tiles;
+  if (splits > kblk) splits = kblk;
+  if (splits < 1) splits = 1;
+  const int64_t per = (kblk + splits - 1) / splits;
+  p.splits = (int)((kblk + per - 1) / per);
+  p.kc = (int)(per * 64);
+  p.kpad = (int64_t)p.splits * p.kc;
+  p.nblk = (L + kTile - 1) / kTile;
+  int64_t off = 0;
+  p.off_dyT = off; off += al(d * p.kpad * 2);
+  p.off_eT = off;  off += al(E * p.kpad * 2);
+  p.off_WT = off;  off += al(E * d * 2);
+  p.off_part = off; off += al((int64_t)p.splits * d * E * 4);
+  p.off_k0 = off; off += al(L * 4);
+  p.off_k1 = off; off += al(L * 4);
+  p.off_v0 = off; off += al(L * 4);
+  p.off_v1 = off; off += al(L * 4);
+  p.off_counts = off; off += al((kDigits * p.nblk + 16) * 4);
+  p.off_flags = off; off += al(L * 4);
+  p.off_seg = off; off += al((L + 1) * 4);
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_backward_scalar(const DevLayout& Ly, const BackwardPlan& p, float g,
+                                  const int64_t* rows, const uint64_t* signs, const void* e,
+                                  const void* dy, const void* W, int64_t N, int64_t d,
+                                  float* dW, float* de, int64_t* urows, float* ugrad,
+                                  int64_t* n_unique, void* workspace, hipStream_t s) {
+  const int OK = Ly.O * Ly.K;
+  const int r = Ly.r;
+  const int64_t E = (int64_t)OK * r;
+  const int64_t L = N * OK;
+  auto* ws = static_cast<uint8_t*>(workspace);
+  auto* dyT = reinterpret_cast<uint16_t*>(ws + p.off_dyT);
+  auto* eT = reinterpret_cast<uint16_t*>(ws + p.off_eT);
+  auto* WT = reinterpret_cast<uint16_t*>(ws + p.off_WT);
+  auto* part = reinterpret_cast<float*>(ws + p.off_part);
+  auto* k0 = reinterpret_cast<uint32_t*>(ws + p.off_k0);
+  auto* k1 = reinterpret_cast<uint32_t*>(ws + p.off_k1);
+  auto* v0 = reinterpret_cast<int32_t*>(ws + p.off_v0);
+  auto* v1 = reinterpret_cast<int32_t*>(ws + p.off_v1);
+  auto* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
+  auto* total = counts + kDigits * p.nblk;
+  auto* flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
+  auto* seg = reinterpret_cast<int32_t*>(ws + p.off_seg);
+  const auto* dyb = static_cast<const uint16_t*>(dy);
+  const auto* eb = static_cast<const uint16_t*>(e);
+  const auto* Wb = static_cast<const uint16_t*>(W);
+
+  // de = g dy W: A = dy [N][d], B = W^T [E][d]
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((E + 63) / 64)),
+                     dim3(kThreads), 0, s, Wb, d, E, E, WT, d, d);
+  hipError_t err = launch_gemm_f32(dy, (int)d, WT, (int)d, N, (int)E, (int)d, 1, g, de, E, s);
+  if (err != hipSuccess) return err;
+  // dW = g dy^T e: A = dy^T [d][kpad], B = e^T [E][kpad], split K
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(p.kpad / 64), (unsigned)((d + 63) / 64)),
+                     dim3(kThreads), 0, s, dyb, N, d, d, dyT, p.kpad, p.kpad);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(p.kpad / 64), (unsigned)((E + 63) / 64)),
+                     dim3(kThreads), 0, s, eb, N, E, E, eT, p.kpad, p.kpad);
+  err = launch_gemm_f32(dyT, (int)p.kpad, eT, (int)p.kpad, d, (int)E, p.kc, p.splits, g, part, E, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid_for(d * E, kThreads)), dim3(kThreads), 0, s,
+                     part, p.splits, d * E, dW);
+
+  // sort the lookups by row (stable), digits of the row index up to R
+  hipLaunchKernelGGL(sort_init_kernel, dim3(grid_for(L, kThreads)), dim3(kThreads), 0, s, rows,
+                     L, k0, v0);
+  int bits = 1;
+  while (bits < 32 && ((uint64_t)1 << bits) < (uint64_t)Ly.n_rows) ++bits;
+  uint32_t* ka = k0;
+  uint32_t* kb = k1;
+  int32_t* va = v0;
+  int32_t* vb = v1;
+  for (int shift = 0; shift < bits; shift += kRadixBits) {
+    hipLaunchKernelGGL(radix_hist_kernel, dim3((unsigned)p.nblk), dim3(kThreads), 0, s, ka, L,
+                       shift, counts);
+    hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kThreads), 0, s, counts,
+                       (int64_t)kDigits * p.nblk, total);
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)p.nblk), dim3(kThreads), 0, s, ka, va,
+                       L, shift, counts, kb, vb);
+    uint32_t* tk = ka; ka = kb; kb = tk;
+    int32_t* tv = va; va = vb; vb = tv;
+  }
+  // segments of equal rows and their sums
+  hipLaunchKernelGGL(seg_flags_kernel, dim3((unsigned)p.nblk), dim3(kThreads), 0, s, ka, L,
+                     flags, counts);
+  hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kThreads), 0, s, counts, p.nblk, total);
+  hipLaunchKernelGGL(seg_starts_kernel, dim3((unsigned)p.nblk), dim3(kThreads), 0, s, flags, L,
+                     counts, total, seg, n_unique);
+  hipLaunchKernelGGL(seg_reduce_kernel, dim3(grid_for(L, kThreads / 64)), dim3(kThreads), 0, s,
+                     ka, va, seg, n_unique, OK, r, Ly.W, Ly.use_signs, de, signs, urows, ugrad);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t s) {
+  hipLaunchKernelGGL(set_i64_kernel, dim3(1), dim3(1), 0, s, p, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_step(const int64_t* urows, const float* ugrad, const int64_t* n_unique,
+                           int64_t max_unique, int r, float* table, float* vhat, int64_t* last,
+                           int64_t step, float lr, float beta2, float wd, float eps,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(rms_step_kernel, dim3(grid_for(max_unique, kThreads / 64)), dim3(kThreads), 0,
+                     s, urows, ugrad, n_unique, r, table, vhat, last, step, lr, beta2, wd, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_flush(int64_t R, int r, float* table, float* vhat, int64_t* last,
+                            int64_t step, float lr, float beta2, float wd, hipStream_t s) {
+  hipLaunchKernelGGL(rms_flush_kernel, dim3(grid_for(R, kThreads)), dim3(kThreads), 0, s, R, r,
+                     table, vhat, last, step, lr, beta2, wd);
+  return hipGetLastError();
+}
+
+}  // namespace pg

@@ -179,6 +179,36 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
                                  const void* W, int64_t d, float g, const void* resid,
                                  void* out, hipStream_t s);
 
+// fp32-output GEMM with optional split K (partials at out + s * M * ldo).
+hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64_t M, int N,
+                           int Kc, int splits, float g, float* out, int64_t ldo,
+                           hipStream_t s);
+
+// Backward pass of the scalar gate and the sparse table update
+// (backward.hip): workspace geometry, then the launchers.
+struct BackwardPlan {
+  int splits;       // K splits of the dW GEMM
+  int kc;           // tokens per split (multiple of 64)
+  int64_t kpad;     // splits * kc: padded token count of the transposes
+  int64_t nblk;     // blocks of the sort / segment kernels
+  int64_t off_dyT, off_eT, off_WT, off_part, off_k0, off_k1, off_v0, off_v1, off_counts,
+      off_flags, off_seg;
+  int64_t bytes;
+};
+BackwardPlan backward_plan(int64_t N, int64_t d, int64_t E, int64_t L);
+hipError_t launch_backward_scalar(const DevLayout& L, const BackwardPlan& p, float g,
+                                  const int64_t* rows, const uint64_t* signs, const void* e,
+                                  const void* dy, const void* W, int64_t N, int64_t d,
+                                  float* dW, float* de, int64_t* urows, float* ugrad,
+                                  int64_t* n_unique, void* workspace, hipStream_t s);
+hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t s);
+hipError_t launch_rms_step(const int64_t* urows, const float* ugrad, const int64_t* n_unique,
+                           int64_t max_unique, int r, float* table, float* vhat, int64_t* last,
+                           int64_t step, float lr, float beta2, float wd, float eps,
+                           hipStream_t s);
+hipError_t launch_rms_flush(int64_t R, int r, float* table, float* vhat, int64_t* last,
+                            int64_t step, float lr, float beta2, float wd, hipStream_t s);
+
 // Engram fusion (bf16): workspace layout described in engram_workspace_bytes.
 int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M);
 hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,

@@ -55,7 +55,7 @@ constexpr int kColBlock = 256;   // Engram partial-sum column block
 constexpr int kPipeBK = 64;      // K stage of the pipelined kernel
 constexpr int kPipeStages = 2;   // its LDS ring
 
-enum { EPI_SCALAR = 0, EPI_ENGRAM = 1 };
+enum { EPI_SCALAR = 0, EPI_ENGRAM = 1, EPI_F32 = 2 };
 
 struct EpiArgs {
   // scalar gate
@@ -71,6 +71,13 @@ struct EpiArgs {
   float* part_k;           // [Mbr][3][n_cb][M]
   const float* gamma_h;
   const float* gamma_k;
+  // fp32 output (g * acc): out_f32[row * ldo + col]; with split K, block
+  // column blockIdx.y covers K range [y K, (y+1) K) of the operands and
+  // writes its partial product at out_f32 + y * M * ldo
+  float* out_f32;
+  int64_t ldo;
+  // operand row strides in elements (0: K)
+  int lda, ldb;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -199,6 +206,13 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLdsBytes];
 
+  const int64_t lda = ep.lda ? ep.lda : K;
+  const int64_t ldb = ep.ldb ? ep.ldb : K;
+  if constexpr (EPI == EPI_F32) {
+    A += (int64_t)blockIdx.y * K;
+    Bw += (int64_t)blockIdx.y * K;
+  }
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -226,6 +240,11 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     pre_src = ep.resid;
     pre_ld = N;
     pre_c0 = n0;
+  } else if constexpr (EPI == EPI_F32) {
+    pre_ok = false;
+    pre_src = nullptr;
+    pre_ld = 0;
+    pre_c0 = 0;
   } else {
     const int seg = n0 / ep.d;
     pre_ok = seg > 0;
@@ -248,23 +267,24 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   // (a group's first row is a multiple of RPI, so swz(row) = swz(dr))
   const uint32_t chunk_b = (uint32_t)((dpos ^ swz(dr)) * 16);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_rows = [&](const uint16_t* mat, int64_t rows, int64_t r0, int kt, uint32_t lds) {
+  auto issue_rows = [&](const uint16_t* mat, int64_t ld, int64_t rows, int64_t r0, int kt,
+                        uint32_t lds) {
     int64_t rb = r0 < rows ? r0 : rows - 1;
     const int lim = (int)(rows - 1 - rb);
     const int rr = dr < lim ? dr : lim;
-    dma16(mat + rb * K + kt * BK, (uint32_t)(rr * K * 2) + chunk_b, lds);
+    dma16(mat + rb * ld + kt * BK, (uint32_t)(rr * ld * 2) + chunk_b, lds);
   };
   auto issue_a_part = [&](int kt, int j0, int j1) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
     for (int j = j0; j < j1; ++j)
-      issue_rows(A, M, m0 + (wave * A_DMA + j) * RPI, kt, la + j * 1024);
+      issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, kt, la + j * 1024);
   };
   auto issue_b_part = [&](int kt, int j0, int j1) {
     const uint32_t lb = lds0 + Cfg::kBOffset + (kt % S) * Cfg::kBBytes + wave * B_DMA * 1024;
 #pragma unroll
     for (int j = j0; j < j1; ++j)
-      issue_rows(Bw, N, n0 + (wave * B_DMA + j) * RPI, kt, lb + j * 1024);
+      issue_rows(Bw, ldb, N, n0 + (wave * B_DMA + j) * RPI, kt, lb + j * 1024);
   };
   auto issue_a = [&](int kt) { issue_a_part(kt, 0, A_DMA); };
   auto issue_b = [&](int kt) { issue_b_part(kt, 0, B_DMA); };
@@ -448,7 +468,31 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   };
   // The full-tile path is one straight line of passes (no join with the
   // edge path, whose loads would make every pass wait for earlier stores).
-  if constexpr (EPI == EPI_SCALAR) {
+  if constexpr (EPI == EPI_F32) {
+    float* obase0 = ep.out_f32 + (int64_t)blockIdx.y * M * ep.ldo;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      stage(p);
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int idx = tid + it * kThreads;
+        const int64_t row = m0 + p * R + idx / CPR;
+        const int col = n0 + (idx % CPR) * 8;
+        float y[8], xin[8];
+        item_y(p, it, y, xin);
+        if (row >= M) continue;
+        float* o = obase0 + row * ep.ldo + col;
+        if (col + 8 <= N && (ep.ldo & 3) == 0) {
+          *reinterpret_cast<float4*>(o) =
+              make_float4(ep.g * y[0], ep.g * y[1], ep.g * y[2], ep.g * y[3]);
+          *reinterpret_cast<float4*>(o + 4) =
+              make_float4(ep.g * y[4], ep.g * y[5], ep.g * y[6], ep.g * y[7]);
+        } else {
+          for (int u = 0; u < 8 && col + u < N; ++u) o[u] = ep.g * y[u];
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_SCALAR) {
     if (full) {
       // Addresses: a wave-uniform row base per pass plus a 32-bit element
       // offset per item (the pass is R rows of N elements).
@@ -704,10 +748,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
 // BM x BN tiles, K stages of BK through a ring of S, MINB blocks per CU.
 template <int BM, int BN, int BK, int S, int MINB, int EPI>
 hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
-                       const EpiArgs& ep, hipStream_t s) {
+                       const EpiArgs& ep, hipStream_t s, int splits = 1) {
   static_assert(PipeCfg<BM, BN, BK, S>::kLdsBytes * MINB <= 160 * 1024, "LDS per CU");
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB>),
+                     dim3((unsigned)blocks, (unsigned)splits),
                      dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
                      static_cast<const uint16_t*>(W), M, N, K, ep);
   return hipGetLastError();
@@ -745,6 +790,21 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
                      static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), N,
                      (int)d, (int)E, ep);
   return hipGetLastError();
+}
+
+// out[s][M][N] (fp32, row stride ldo) = g * A[M][s Kc .. (s+1) Kc) . B[N][same]^T
+// for s < splits: bf16 operands with row strides lda / ldb; Kc a multiple of
+// 64 (checked by the caller).
+hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64_t M, int N,
+                           int Kc, int splits, float g, float* out, int64_t ldo,
+                           hipStream_t s) {
+  EpiArgs ep{};
+  ep.g = g;
+  ep.out_f32 = out;
+  ep.ldo = ldo;
+  ep.lda = lda;
+  ep.ldb = ldb;
+  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_F32>(A, M, N, Kc, B, ep, s, splits);
 }
 
 // Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller).

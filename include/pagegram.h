@@ -262,6 +262,79 @@ PG_API int64_t pg_workspace_size(const pg_layout* layout, const pg_fuse* fuse,
                                  int64_t B, int64_t T);
 
 /* ------------------------------------------------------------------------
+ * Backward pass of the scalar-gated path and the sparse table update
+ * (PageGram tech report §3.3: tables start at zero, a row-wise adaptive RMS
+ * optimiser with replayed decay; §9.1: beta2 = 0.95; §9.4 check 4: the
+ * sparse gradient equals the dense one). Readings where the pages are
+ * silent: v is one scalar per row (moving average of the row's mean squared
+ * gradient), no bias correction, a step divides by sqrt(v) + eps and applies
+ * decoupled weight decay.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * pg_backward_workspace_size -- device workspace bytes of pg_backward_scalar
+ * for B x T tokens (negative pg_status for unsupported shapes: the scalar
+ * gate, bf16 activations, d a multiple of 64, e_dim a multiple of 8, fewer
+ * than 2^31 lookups and 2^32 rows).
+ */
+PG_API int64_t pg_backward_workspace_size(const pg_layout* layout, const pg_fuse* fuse,
+                                          int64_t B, int64_t T);
+
+/*
+ * pg_backward_scalar -- gradients of out = x + g W e (fuse->g) given
+ * dy = dL/dout:
+ *   de  fp32 [B*T][e_dim] = g dy W
+ *   dW  fp32 [d][e_dim]   = g dy^T e  (summed over tokens in a fixed order)
+ *   table gradient restricted to the touched rows: urows int64 [*n_unique]
+ *   ascending, ugrad fp32 [*n_unique][r]; ugrad[u] is the sum over the
+ *   lookups (t, n, k) with rows[t][n][k] = urows[u], in lookup order, of
+ *   s_{t,n,k} (.) de[t][(n,k) slice].
+ *   rows, signs: pg_index's outputs for these tokens; e: the forward's e
+ *   (bf16 [B*T][e_dim]); dy bf16 [B*T][d]; W bf16 [d][e_dim] (device).
+ *   urows / ugrad need room for B*T*O*K entries; n_unique is a device int64.
+ * Deterministic (no floating-point atomics). Errors: PG_EUNSUPPORTED for the
+ * shapes pg_backward_workspace_size rejects, PG_EINVAL for NULL or
+ * misaligned (16 B) pointers or a short workspace (256-byte aligned).
+ */
+PG_API int pg_backward_scalar(const pg_layout* layout, const pg_fuse* fuse,
+                              const int64_t* rows, const uint64_t* signs, const void* e,
+                              const void* dy, const void* W, int64_t B, int64_t T,
+                              float* dW, float* de, int64_t* urows, float* ugrad,
+                              int64_t* n_unique, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * pg_row_rms_step -- one optimiser step at step number `step` (>= 1) on the
+ * rows urows[0 .. *n_unique) with gradients ugrad (pg_backward_scalar's
+ * outputs; max_unique bounds *n_unique). For a row last updated at step
+ * tau (last_step[row], 0 when never), with k = step - tau:
+ *   v     <- beta2^k v + (1 - beta2) mean_j(g_j^2)
+ *   theta <- theta (1 - lr wd)^k - lr g / (sqrt(v) + eps)
+ *   last_step[row] <- step
+ * (the k - 1 skipped steps replayed as decay, then this step).
+ *   table fp32 [R][r] (the master copy of the table), vhat fp32 [R],
+ *   last_step int64 [R] (device; zero-initialised by the caller).
+ * Errors: PG_EINVAL for bad hyper-parameters (beta2 outside [0, 1),
+ * lr * wd >= 1, negative values) or NULL pointers.
+ */
+PG_API int pg_row_rms_step(const pg_layout* layout, const int64_t* urows,
+                           const float* ugrad, const int64_t* n_unique, int64_t max_unique,
+                           float* table, float* vhat, int64_t* last_step, int64_t step,
+                           float lr, float beta2, float weight_decay, float eps,
+                           hipStream_t stream);
+
+/*
+ * pg_row_rms_flush -- brings every row to `step`: theta *= (1 - lr wd)^k,
+ * v *= beta2^k, last_step = step, with k = step - last_step[row] (rows
+ * already at step untouched). After it the table equals the one a dense
+ * optimiser (every row every step, zero gradients for untouched rows)
+ * would hold.
+ */
+PG_API int pg_row_rms_flush(const pg_layout* layout, float* table, float* vhat,
+                            int64_t* last_step, int64_t step, float lr, float beta2,
+                            float weight_decay, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Flash page-cache simulation (host code; PageGram tech report §2.3, §3.3,
  * §8 Fig. 4a and appendix D). A table kept on flash is read in 4 KiB blocks;
  * a RAM page cache with LRU replacement holds whole blocks; each lookup whose
