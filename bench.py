@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (for counter scaling)")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (pg_backward_scalar) and the row-wise RMS "
+                        "table update (pg_row_rms_step) on the workload")
     p.add_argument("--page-cache", action="store_true",
                    help="flash page-cache figures (reads/token under an LRU RAM cache) "
                         "of the 20B NF4 table in the PageGram S=4, S=15 and Engram-style "
@@ -205,6 +208,94 @@ def page_cache(batches):
     return res
 
 
+def backward_bench(args):
+    """Backward pass + sparse table update of a scalar-gate workload: K
+    back-to-back calls of each entry point between HIP events."""
+    import numpy as np
+    import torch
+
+    import hashed_head_gram_amd as pg
+    import synth
+    from synth import configs, device as sdev
+
+    dev = torch.device("cuda:0")
+    wl = configs.workload(args.workload)
+    lay_d = wl["layout"]
+    layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
+                            pages=lay_d["pages"], head_rows=lay_d["head_rows"],
+                            hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
+                            n_min=lay_d["n_min"], n_max=lay_d["n_max"],
+                            pad_id=wl["canon_vocab"])
+    R = pg.pg_layout_rows(layout)
+    r, K = lay_d["r"], lay_d["K"]
+    O = lay_d["n_max"] - lay_d["n_min"] + 1
+    B, T = wl["B"], wl["T"]
+    N, E, d = B * T, O * K * r, wl["d"]
+    L = N * O * K
+    tab = torch.empty(R, r, dtype=torch.bfloat16, device=dev)
+    sdev.fill_normal(tab, wl["table_seed"], configs.STREAM_TABLE, wl["table_sigma"])
+    table = pg.make_table(pg.PG_BF16, tab, R)
+    cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
+    toks = torch.from_numpy(synth.tokens(wl)).to(dev)
+    W = torch.empty(d, E, dtype=torch.bfloat16, device=dev)
+    sdev.fill_normal(W, wl["data_seed"], configs.STREAM_W, wl["w_sigma"])
+    dy = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+    sdev.fill_normal(dy, wl["data_seed"] + 1000, configs.STREAM_RESID, 0.1)
+    rows = torch.empty(N, O, K, dtype=torch.int64, device=dev)
+    signs = torch.empty(N, O, K, (r + 63) // 64, dtype=torch.int64, device=dev)
+    e = torch.empty(N, E, dtype=torch.bfloat16, device=dev)
+    pg.pg_index(layout, toks, cmap, rows, signs)
+    pg.pg_index_gather(layout, table, toks, cmap, pg.PG_BF16, e)
+    f = pg.make_fuse(pg.PG_GATE_SCALAR, pg.PG_BF16, d, g=wl["g"])
+    ws = torch.empty(pg.pg_backward_workspace_size(layout, f, B, T), dtype=torch.uint8,
+                     device=dev)
+    dW = torch.empty(d, E, dtype=torch.float32, device=dev)
+    de = torch.empty(N, E, dtype=torch.float32, device=dev)
+    urows = torch.empty(L, dtype=torch.int64, device=dev)
+    ugrad = torch.empty(L, r, dtype=torch.float32, device=dev)
+    nu = torch.zeros(1, dtype=torch.int64, device=dev)
+    master = torch.zeros(R, r, dtype=torch.float32, device=dev)
+    vhat = torch.zeros(R, dtype=torch.float32, device=dev)
+    last = torch.zeros(R, dtype=torch.int64, device=dev)
+
+    def bwd():
+        pg.pg_backward_scalar(layout, f, rows, signs, e, dy, W, B, T, dW, de, urows, ugrad,
+                              nu, ws)
+    step_no = [0]
+
+    def upd():
+        step_no[0] += 1
+        pg.pg_row_rms_step(layout, urows, ugrad, nu, L, master, vhat, last, step_no[0],
+                           1e-2, 0.95, 0.0, 1e-8)
+
+    def per_call_ms(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    bw_ms = per_call_ms(bwd, args.steps)
+    up_ms = per_call_ms(upd, args.steps)
+    n_unique = int(nu.item())
+    gemm_flops = 2 * 2 * N * d * E
+    return {"metric": "backward + sparse table update time per step", "unit": "ms",
+            "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "dtype": "bf16 operands, fp32 gradients and master table",
+            "data": "synthetic (seeded Zipf tokens, counter-generated table, W and dy)",
+            "config": {"workload": wl["name"], "tokens": N, "lookups": L, "d": d, "e_dim": E,
+                       "table_rows": R},
+            "pg_backward_scalar_ms": bw_ms, "pg_row_rms_step_ms": up_ms,
+            "distinct_rows": n_unique,
+            "gemm_flops": gemm_flops,
+            "gemm_only_TFLOPs_if_whole_call": gemm_flops / (bw_ms / 1e3) / 1e12,
+            "backward_tokens_per_s": N / ((bw_ms + up_ms) / 1e3)}
+
+
 def cpu_baseline(wl, n_tok):
     """The CPU oracle on the first n_tok tokens of the workload's stream."""
     import numpy as np
@@ -273,6 +364,9 @@ def main():
     args = parse()
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
+        return
+    if args.backward:
+        print(json.dumps(backward_bench(args)), flush=True)
         return
     if args.page_cache:
         line = {"metric": "flash reads per token under an LRU RAM page cache (4 KiB blocks)",

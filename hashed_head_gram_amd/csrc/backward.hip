@@ -6,10 +6,13 @@
 //   dW = g dy^T e               (split-K GEMM over tokens, fp32 partials,
 //                                reduced in split order)
 //   table gradient: lookups (t, n, k) sorted by row with a stable LSD radix
-//   sort (4-bit digits), then one wave per distinct row sums
+//   sort (4-bit digits), then a 16-lane group per distinct row sums
 //   s_{t,n,k} (.) de[t][(n,k) slice] over its lookups in sorted order, which
-//   is lookup order (stable sort) -- deterministic, no atomics on values.
-//   step: one wave per distinct row applies the replayed decay of the steps
+//   is lookup order (stable sort); rows with more than 16 lookups (hot
+//   n-grams: a few hundred lookups under Zipf text) go to a whole block each,
+//   summed per lane group and then across groups in a fixed order --
+//   deterministic either way, no atomics on values.
+//   step: 16 lanes per distinct row apply the replayed decay of the steps
 //   the row missed and the RMS step of this one.
 #include "common.h"
 
@@ -62,10 +65,12 @@ __global__ __launch_bounds__(kThreads) void reduce_splits_kernel(
 // Block b owns items [b * kTile, (b+1) * kTile); thread t of it owns the
 // kItems consecutive items starting at b * kTile + t * kItems.
 
-// keys[i] (row as uint32) and vals[i] = i for the lookups.
+// keys[i] (row as uint32) and vals[i] = i for the lookups; clears the
+// long-segment counter used by the segment reduction.
 __global__ __launch_bounds__(kThreads) void sort_init_kernel(
     const int64_t* __restrict__ rows, int64_t n, uint32_t* __restrict__ keys,
-    int32_t* __restrict__ vals) {
+    int32_t* __restrict__ vals, int32_t* __restrict__ n_long) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_long = 0;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads) {
     keys[i] = (uint32_t)rows[i];
@@ -145,8 +150,8 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     F[d * kThreads + t] = cnt;
   }
   __syncthreads();
-  // exclusive scan of F (digit-major, 4096 entries): thread j owns 16
-  // consecutive entries, all of digit j / 16
+  // exclusive scan of F (digit-major, kDigits * kThreads entries): thread j
+  // owns kDigits consecutive entries, all of digit j * kDigits / kThreads
   int32_t loc[kDigits];
   int32_t run = 0;
 #pragma unroll
@@ -247,41 +252,176 @@ __global__ __launch_bounds__(kThreads) void seg_starts_kernel(
   }
 }
 
-// One wave per distinct row: urows[s], ugrad[s][0..r) = sum over its lookups
-// (sorted order) of sign * de slice.
+// Per-row gradient sums. A row's lookups are contiguous in the sorted
+// order; ugrad[s][0..r) = sum over them, in that order, of sign (.) de slice.
+// Lanes of a 16-lane group cover V-element chunks of the row (V = 4 when
+// r % 4 == 0, else 1): chunk c0 + lane, c0 + 16 + lane, ...
+constexpr int kRowLanes = 16;
+constexpr int kGroups = kThreads / kRowLanes;      // lane groups per block
+constexpr int kShortMax = 16;                      // longest segment of one group
+
+template <int V>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ p, float (&x)[V]) {
+  if constexpr (V == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  } else {
+    x[0] = *p;
+  }
+}
+
+template <int V>
+__device__ __forceinline__ void store_chunk(float* __restrict__ p, const float (&x)[V]) {
+  if constexpr (V == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else {
+    *p = x[0];
+  }
+}
+
+// acc += sign (.) x, where bits holds the V sign bits of the chunk (bit set:
+// negate); the chunk never crosses a 64-bit sign word since V divides 64.
+template <int V>
+__device__ __forceinline__ void add_signed(float (&acc)[V], const float (&x)[V], uint32_t bits) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] += ((bits >> v) & 1u) ? -x[v] : x[v];
+}
+
+// One group per segment of at most kShortMax lookups: each lane fetches one
+// lookup index, the group broadcasts them and keeps four row loads in
+// flight. Longer segments are appended to long_list (after the counter at
+// long_list[0]) for seg_reduce_long_kernel.
+template <int V>
 __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(
     const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
     const int32_t* __restrict__ seg_start, const int64_t* __restrict__ n_unique, int OK, int r,
     int W, int use_signs, const float* __restrict__ de, const uint64_t* __restrict__ signs,
-    int64_t* __restrict__ urows, float* __restrict__ ugrad) {
-  const int64_t sidx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (sidx >= *n_unique) return;
+    int64_t* __restrict__ urows, float* __restrict__ ugrad, int32_t* __restrict__ long_list) {
+  const int64_t sidx = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kRowLanes;
+  const int ln = threadIdx.x % kRowLanes;
+  const int gbase = (int)(threadIdx.x % 64) - ln;   // first lane of the group in its wave
+  if (sidx >= *n_unique) return;                    // the whole group leaves together
   const int32_t i0 = seg_start[sidx], i1 = seg_start[sidx + 1];
+  const int len = i1 - i0;
+  if (ln == 0) urows[sidx] = (int64_t)keys[i0];
+  if (len > kShortMax) {
+    if (ln == 0) long_list[1 + atomicAdd(long_list, 1)] = (int32_t)sidx;
+    return;
+  }
   const int64_t E = (int64_t)OK * r;
-  if (lane == 0) urows[sidx] = (int64_t)keys[i0];
-  for (int j0 = 0; j0 < r; j0 += 64) {
-    const int j = j0 + lane;
-    if (j >= r) break;
-    float acc = 0.f;
-    for (int32_t i = i0; i < i1; ++i) {
-      const int64_t q = vals[i];
-      const int64_t tok = q / OK;
-      const int slot = (int)(q - tok * OK);
-      float x = de[tok * E + (int64_t)slot * r + j];
-      if (use_signs && ((signs[q * W + (j >> 6)] >> (j & 63)) & 1ull)) x = -x;
-      acc += x;
+  const uint32_t q = ln < len ? (uint32_t)vals[i0 + ln] : 0u;
+  const uint32_t tok = q / (uint32_t)OK;
+  const int64_t base = (int64_t)tok * E + (int64_t)(q - tok * (uint32_t)OK) * r;
+  const int nc = r / V;
+  for (int c0 = 0; c0 < nc; c0 += kRowLanes) {     // trip count uniform in the group
+    const int c = c0 + ln;
+    const bool act = c < nc;
+    const int j = act ? c * V : 0;
+    float acc[V] = {};
+    for (int k = 0; k < len; k += 4) {             // len uniform in the group
+      float x[4][V];
+      uint32_t sb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t b = __shfl(base, gbase + ((k + u) & 15), 64);
+        const uint32_t qq = __shfl(q, gbase + ((k + u) & 15), 64);
+        sb[u] = 0u;
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[u][v] = 0.f;
+        if (act && k + u < len) {
+          load_chunk<V>(de + b + j, x[u]);
+          if (use_signs)
+            sb[u] = (uint32_t)(signs[(int64_t)qq * W + (j >> 6)] >> (j & 63)) & ((1u << V) - 1u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k + u < len) add_signed<V>(acc, x[u], sb[u]);
     }
-    ugrad[sidx * r + j] = acc;
+    if (act) store_chunk<V>(ugrad + sidx * r + j, acc);
+  }
+}
+
+// One block per long segment (list from seg_reduce_kernel; entries in any
+// order, each summed by one block in a fixed order): the block stages up to
+// 256 lookups at a time in LDS, group g sums lookups g, g + 16, ... of the
+// segment in order, then group 0 adds the 16 group sums in group order.
+template <int V>
+__global__ __launch_bounds__(kThreads) void seg_reduce_long_kernel(
+    const int32_t* __restrict__ vals, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ long_list, int OK, int r, int W, int use_signs,
+    const float* __restrict__ de, const uint64_t* __restrict__ signs,
+    float* __restrict__ ugrad) {
+  __shared__ int64_t sbase[kThreads];
+  __shared__ uint32_t sq[kThreads];
+  __shared__ float red[kGroups][kRowLanes][V];
+  const int grp = threadIdx.x / kRowLanes, ln = threadIdx.x % kRowLanes;
+  const int n_long = long_list[0];
+  const int64_t E = (int64_t)OK * r;
+  const int nc = r / V;
+  for (int li = blockIdx.x; li < n_long; li += gridDim.x) {     // uniform in the block
+    const int64_t sidx = long_list[1 + li];
+    const int32_t i0 = seg_start[sidx], i1 = seg_start[sidx + 1];
+    for (int c0 = 0; c0 < nc; c0 += kRowLanes) {
+      const int c = c0 + ln;
+      const bool act = c < nc;
+      const int j = act ? c * V : 0;
+      float acc[V] = {};
+      for (int32_t b0 = i0; b0 < i1; b0 += kThreads) {
+        __syncthreads();                            // previous batch fully read
+        const int32_t i = b0 + (int32_t)threadIdx.x;
+        if (i < i1) {
+          const uint32_t q = (uint32_t)vals[i];
+          const uint32_t tok = q / (uint32_t)OK;
+          sbase[threadIdx.x] = (int64_t)tok * E + (int64_t)(q - tok * (uint32_t)OK) * r;
+          sq[threadIdx.x] = q;
+        }
+        __syncthreads();
+        const int cnt = i1 - b0 < kThreads ? i1 - b0 : kThreads;
+        for (int k = grp; k < cnt; k += 4 * kGroups) {
+          float x[4][V];
+          uint32_t sb[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = k + u * kGroups;
+            sb[u] = 0u;
+#pragma unroll
+            for (int v = 0; v < V; ++v) x[u][v] = 0.f;
+            if (act && e < cnt) {
+              load_chunk<V>(de + sbase[e] + j, x[u]);
+              if (use_signs)
+                sb[u] = (uint32_t)(signs[(int64_t)sq[e] * W + (j >> 6)] >> (j & 63)) &
+                        ((1u << V) - 1u);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k + u * kGroups < cnt) add_signed<V>(acc, x[u], sb[u]);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) red[grp][ln][v] = acc[v];
+      __syncthreads();
+      if (grp == 0 && act) {
+        float sum[V] = {};
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int v = 0; v < V; ++v) sum[v] += red[g][ln][v];
+        store_chunk<V>(ugrad + sidx * r + j, sum);
+      }
+      __syncthreads();                              // red reused by the next chunk
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Row-wise RMS step and flush.
 
-__device__ __forceinline__ float wave_sum(float x) {
+// sum over the 16 lanes of a row group (fixed xor tree: deterministic)
+__device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) x += __shfl_xor(x, sh, 64);
+  for (int sh = kRowLanes / 2; sh >= 1; sh >>= 1) x += __shfl_xor(x, sh, 64);
   return x;
 }
 
@@ -290,22 +430,26 @@ __global__ __launch_bounds__(kThreads) void rms_step_kernel(
     const int64_t* __restrict__ n_unique, int r, float* __restrict__ table,
     float* __restrict__ vhat, int64_t* __restrict__ last, int64_t step, float lr, float beta2,
     float wd, float eps) {
-  const int64_t sidx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (sidx >= *n_unique) return;
-  const int64_t row = urows[sidx];
-  const float* g = ugrad + sidx * r;
+  const int64_t sidx = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kRowLanes;
+  const int ln = threadIdx.x % kRowLanes;
+  // every lane of a 16-lane group takes part in the group sum: a group past
+  // n_unique computes on row 0 of its own (unwritten) slot range and stores
+  // nothing
+  const bool live = sidx < *n_unique;
+  const int64_t row = live ? urows[sidx] : 0;
+  const float* g = ugrad + (live ? sidx : 0) * r;
   float ss = 0.f;
-  for (int j = lane; j < r; j += 64) ss += g[j] * g[j];
-  const float m = wave_sum(ss) / (float)r;
+  for (int j = ln; j < r; j += kRowLanes) ss += live ? g[j] * g[j] : 0.f;
+  const float m = group_sum(ss) / (float)r;
+  if (!live) return;
   int64_t k = step - last[row];
   if (k < 1) k = 1;
   const float v = powf(beta2, (float)k) * vhat[row] + (1.0f - beta2) * m;
   const float decay = powf(1.0f - lr * wd, (float)k);
   const float inv = lr / (sqrtf(v) + eps);
   float* th = table + row * r;
-  for (int j = lane; j < r; j += 64) th[j] = th[j] * decay - inv * g[j];
-  if (lane == 0) {
+  for (int j = ln; j < r; j += kRowLanes) th[j] = th[j] * decay - inv * g[j];
+  if (ln == 0) {
     vhat[row] = v;
     last[row] = step;
   }
@@ -364,6 +508,7 @@ BackwardPlan backward_plan(int64_t N, int64_t d, int64_t E, int64_t L) {
   p.off_counts = off; off += al((kDigits * p.nblk + 16) * 4);
   p.off_flags = off; off += al(L * 4);
   p.off_seg = off; off += al((L + 1) * 4);
+  p.off_long = off; off += al((L / (kShortMax + 1) + 2) * 4);
   p.bytes = off;
   return p;
 }
@@ -390,6 +535,7 @@ hipError_t launch_backward_scalar(const DevLayout& Ly, const BackwardPlan& p, fl
   auto* total = counts + kDigits * p.nblk;
   auto* flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
   auto* seg = reinterpret_cast<int32_t*>(ws + p.off_seg);
+  auto* long_list = reinterpret_cast<int32_t*>(ws + p.off_long);
   const auto* dyb = static_cast<const uint16_t*>(dy);
   const auto* eb = static_cast<const uint16_t*>(e);
   const auto* Wb = static_cast<const uint16_t*>(W);
@@ -411,7 +557,7 @@ hipError_t launch_backward_scalar(const DevLayout& Ly, const BackwardPlan& p, fl
 
   // sort the lookups by row (stable), digits of the row index up to R
   hipLaunchKernelGGL(sort_init_kernel, dim3(grid_for(L, kThreads)), dim3(kThreads), 0, s, rows,
-                     L, k0, v0);
+                     L, k0, v0, long_list);
   int bits = 1;
   while (bits < 32 && ((uint64_t)1 << bits) < (uint64_t)Ly.n_rows) ++bits;
   uint32_t* ka = k0;
@@ -434,8 +580,20 @@ hipError_t launch_backward_scalar(const DevLayout& Ly, const BackwardPlan& p, fl
   hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kThreads), 0, s, counts, p.nblk, total);
   hipLaunchKernelGGL(seg_starts_kernel, dim3((unsigned)p.nblk), dim3(kThreads), 0, s, flags, L,
                      counts, total, seg, n_unique);
-  hipLaunchKernelGGL(seg_reduce_kernel, dim3(grid_for(L, kThreads / 64)), dim3(kThreads), 0, s,
-                     ka, va, seg, n_unique, OK, r, Ly.W, Ly.use_signs, de, signs, urows, ugrad);
+  // at most L / (kShortMax + 1) segments are long
+  const unsigned long_grid = (unsigned)std::min<int64_t>(L / (kShortMax + 1) + 1, 2048);
+  const dim3 short_grid(grid_for(L, kGroups));
+  if ((r & 3) == 0) {
+    hipLaunchKernelGGL(seg_reduce_kernel<4>, short_grid, dim3(kThreads), 0, s, ka, va, seg,
+                       n_unique, OK, r, Ly.W, Ly.use_signs, de, signs, urows, ugrad, long_list);
+    hipLaunchKernelGGL(seg_reduce_long_kernel<4>, dim3(long_grid), dim3(kThreads), 0, s, va, seg,
+                       long_list, OK, r, Ly.W, Ly.use_signs, de, signs, ugrad);
+  } else {
+    hipLaunchKernelGGL(seg_reduce_kernel<1>, short_grid, dim3(kThreads), 0, s, ka, va, seg,
+                       n_unique, OK, r, Ly.W, Ly.use_signs, de, signs, urows, ugrad, long_list);
+    hipLaunchKernelGGL(seg_reduce_long_kernel<1>, dim3(long_grid), dim3(kThreads), 0, s, va, seg,
+                       long_list, OK, r, Ly.W, Ly.use_signs, de, signs, ugrad);
+  }
   return hipGetLastError();
 }
 
@@ -448,7 +606,7 @@ hipError_t launch_rms_step(const int64_t* urows, const float* ugrad, const int64
                            int64_t max_unique, int r, float* table, float* vhat, int64_t* last,
                            int64_t step, float lr, float beta2, float wd, float eps,
                            hipStream_t s) {
-  hipLaunchKernelGGL(rms_step_kernel, dim3(grid_for(max_unique, kThreads / 64)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(rms_step_kernel, dim3(grid_for(max_unique, kThreads / kRowLanes)), dim3(kThreads), 0,
                      s, urows, ugrad, n_unique, r, table, vhat, last, step, lr, beta2, wd, eps);
   return hipGetLastError();
 }

@@ -192,7 +192,7 @@ struct BackwardPlan {
   int64_t kpad;     // splits * kc: padded token count of the transposes
   int64_t nblk;     // blocks of the sort / segment kernels
   int64_t off_dyT, off_eT, off_WT, off_part, off_k0, off_k1, off_v0, off_v1, off_counts,
-      off_flags, off_seg;
+      off_flags, off_seg, off_long;
   int64_t bytes;
 };
 BackwardPlan backward_plan(int64_t N, int64_t d, int64_t E, int64_t L);
