@@ -13,11 +13,13 @@
 // writes 1 KiB of LDS per instruction; the address is an SGPR base plus a
 // per-lane offset), so no VGPRs are spent on staging. A stage's four K steps
 // interleave: the LDS fragment reads of step s+1 go out between the MFMAs of
-// step s, and the next stage's loads are spread over the steps. The ring is
+// step s; the next stage's loads all go out at the top of the stage. The
+// W fragment is the MFMA's A operand, so each lane's accumulators are runs
+// of four consecutive output columns of one token row. The ring is
 // synchronised with counted vmcnt waits and a bare barrier (a
 // __syncthreads() would drain every outstanding load). The four 16-byte K
-// chunks of a row are XOR-swizzled by the row's low bits so a fragment read
-// is free of bank conflicts. Rows past M or N are clamped in-bounds for the
+// chunks of a row are XOR-swizzled per 256-byte line so a fragment read is
+// free of bank conflicts. Rows past M or N are clamped in-bounds for the
 // loads and never stored.
 //
 // Blocks are renumbered so that each XCD (blocks are dealt round-robin to the
@@ -25,11 +27,12 @@
 // N-major: concurrently running tiles share their E and W panels in one L2.
 //
 // Epilogue: the accumulators are staged through LDS a pass of rows at a
-// time and leave as 16-byte row stores; passes synchronise on LDS only (the
-// stores are never waited for), the bf16 input tile (residual x, or h) is
-// fetched once before the first store, and bf16 packing is one
-// v_cvt_pk_bf16_f32 per pair. Two epilogues: the scalar gate (PageGram §3.1:
-// out = x + g W_V e) and pass 1 of the Engram fusion (Engram notes §3.3-3.4):
+// time (one 16-byte LDS write per four columns) and leave as 16-byte row
+// stores; passes synchronise on LDS only (the stores are never waited for);
+// the bf16 input tile (residual x, or h) is fetched once before the first
+// store; bf16 packing is one v_cvt_pk_bf16_f32 per pair. Two epilogues: the
+// scalar gate (PageGram §3.1: out = x + g W_V e) and pass 1 of the Engram
+// fusion (Engram notes §3.3-3.4):
 // v = W_V e is stored in bf16 and, per token and 256-column block, the
 // partial sums RMSNorm and the context gate need (sum v^2; per branch sum
 // k^2, sum gamma_h gamma_k h k, sum h^2) go to the workspace, so k is never
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA tiles per wave
   constexpr int LPR = BK / 8;                  // 16-byte chunks (lanes) per row
   constexpr int RPI = 64 / LPR;                // rows per DMA instruction
-  constexpr int ROWS_PER_LINE = 64 / BK;       // rows per 128-byte LDS line
+  constexpr int ROWS_PER_LINE = 128 / BK;      // rows per 256-byte LDS line
   constexpr int A_DMA = BM / RPI / 4;          // DMA instructions per wave per stage
   constexpr int B_DMA = BN / RPI / 4;
   constexpr int L = A_DMA + B_DMA;
@@ -253,8 +256,10 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     pre_c0 = n0 - seg * ep.d;
   }
 
-  // Swizzle of the 16-byte chunk position within a row: rows sharing a
-  // 128-byte line, and the next lines, rotate their chunks.
+  // Swizzle of the 16-byte chunk position within a row. gfx950's LDS serves
+  // 256 bytes per clock, so the 16 lanes that a 16-byte read serves together
+  // must hit 16 distinct 16-byte slots of a 256-byte line: the rows sharing
+  // a line differ in their half, and consecutive lines rotate the chunks.
   auto swz = [](int r) { return (r / ROWS_PER_LINE) & (LPR - 1); };
 
   // DMA: lane covers row lane / LPR of an RPI-row slab and LDS chunk position
@@ -264,30 +269,31 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   // rows past the matrix repeat its last row (never stored).
   const int dr = lane / LPR;
   const int dpos = lane % LPR;
-  // (a group's first row is a multiple of RPI, so swz(row) = swz(dr))
+  // A group's first row r0 is a multiple of RPI (and the tile origin a
+  // multiple of 16 rows), so swz(r0 + dr) = swz(r0) ^ swz(dr) with swz(r0)
+  // fixed by the group index.
   const uint32_t chunk_b = (uint32_t)((dpos ^ swz(dr)) * 16);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_rows = [&](const uint16_t* mat, int64_t ld, int64_t rows, int64_t r0, int kt,
-                        uint32_t lds) {
+  auto issue_rows = [&](const uint16_t* mat, int64_t ld, int64_t rows, int64_t r0, int grp,
+                        int kt, uint32_t lds) {
     int64_t rb = r0 < rows ? r0 : rows - 1;
     const int lim = (int)(rows - 1 - rb);
     const int rr = dr < lim ? dr : lim;
-    dma16(mat + rb * ld + kt * BK, (uint32_t)(rr * ld * 2) + chunk_b, lds);
+    dma16(mat + rb * ld + kt * BK,
+          (uint32_t)(rr * ld * 2) + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)), lds);
   };
-  auto issue_a_part = [&](int kt, int j0, int j1) {
+  auto issue_a = [&](int kt) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
-    for (int j = j0; j < j1; ++j)
-      issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, kt, la + j * 1024);
+    for (int j = 0; j < A_DMA; ++j)
+      issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, wave * A_DMA + j, kt, la + j * 1024);
   };
-  auto issue_b_part = [&](int kt, int j0, int j1) {
+  auto issue_b = [&](int kt) {
     const uint32_t lb = lds0 + Cfg::kBOffset + (kt % S) * Cfg::kBBytes + wave * B_DMA * 1024;
 #pragma unroll
-    for (int j = j0; j < j1; ++j)
-      issue_rows(Bw, ldb, N, n0 + (wave * B_DMA + j) * RPI, kt, lb + j * 1024);
+    for (int j = 0; j < B_DMA; ++j)
+      issue_rows(Bw, ldb, N, n0 + (wave * B_DMA + j) * RPI, wave * B_DMA + j, kt, lb + j * 1024);
   };
-  auto issue_a = [&](int kt) { issue_a_part(kt, 0, A_DMA); };
-  auto issue_b = [&](int kt) { issue_b_part(kt, 0, B_DMA); };
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -300,7 +306,10 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   // v_mfma_f32_32x32x16_bf16: lane l holds A row l % 32 (B column l % 32),
   // K elements 8 (l / 32) .. +7 of the 16; D element q of lane l is row
   // 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32. (On gfx950 this form
-  // sustains far more of the bf16 peak than the 16 x 16 x 32 one.)
+  // sustains far more of the bf16 peak than the 16 x 16 x 32 one.) The W
+  // fragment goes in as A and the E fragment as B, so D is the transposed
+  // tile: lane l holds token row l % 32 and, per q / 4, the four consecutive
+  // output columns 8 (q / 4) + 4 (l / 32) + 0..3 -- contiguous in memory.
   const int fr = lane & 31;
   // Fragments of K step s (16 wide, s = 0..3) of stage kt: logical 16-byte
   // chunk 2 s + lane / 32 of row fr of each 32-row tile, stored at that
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
   };
   auto block_sync = [] {
     asm volatile("" ::: "memory");
@@ -330,17 +339,11 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     asm volatile("" ::: "memory");
   };
 
-  // Two-buffer rings for E and W: stage kt+1 is loaded while stage kt is
-  // multiplied. The barrier at the top of step kt means stage kt is in LDS
-  // and every wave is done reading stage kt-1, whose buffers then take
-  // stage kt+1.
   // Rings of S buffers: stage kt+S-1 is loaded while stage kt is multiplied.
   // The barrier at the top of step kt means stage kt is in LDS and every wave
-  // is done reading stage kt-1, whose buffers then take stage kt+S-1. Within
-  // a stage the fragment reads of K step st+1 go out one after each MFMA of
-  // step st (LDS latency hides behind issued matrix work), and the loads of
-  // stage kt+S-1 are spread over the steps so that the wave never stalls on a
-  // burst of load issues while the matrix pipe idles.
+  // is done reading stage kt-1, whose buffers then take stage kt+S-1, issued
+  // right there. Within a stage the fragment reads of K step st+1 go out one
+  // after each MFMA of step st (LDS latency hides behind issued matrix work).
   const int KT = K / BK;
   constexpr int PD = S - 1;                     // stages in flight
   constexpr int NS = BK / 16;                   // K steps per stage
@@ -363,7 +366,12 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     else
       wait_vmcnt<0>();
     block_sync();
-    const bool more = kt + PD < KT;
+    // the stage that reuses the buffers of stage kt-1 goes out at once, so
+    // its load latency overlaps this stage's whole matrix work
+    if (kt + PD < KT) {
+      issue_b(kt + PD);
+      issue_a(kt + PD);
+    }
     bf16x8_t fa[NS][FM], fb[NS][FN];
     load_frags(kt, 0, fa[0], fb[0]);
 #pragma unroll
@@ -380,10 +388,6 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - RD, 0);
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-      }
-      if (more) {
-        issue_a_part(kt + PD, st * A_DMA / NS, (st + 1) * A_DMA / NS);
-        issue_b_part(kt + PD, st * B_DMA / NS, (st + 1) * B_DMA / NS);
       }
     }
   }
@@ -439,13 +443,16 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
     for (int i = 0; i < FM; ++i) {
       // wave-uniform: is this wave's 32-row tile i in pass p?
       if ((wm * WTM + i * 32) / R != p) continue;
+      const int rl = wm * WTM + i * 32 + (lane & 31) - p * R;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rl = wm * WTM + i * 32 + (q >> 2) * 8 + 4 * (lane >> 5) + (q & 3) - p * R;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          tile[rl * RS + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][q];
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = wn * WTN + j * 32 + 8 * g4 + 4 * (lane >> 5);
+          *reinterpret_cast<float4*>(&tile[rl * RS + col]) =
+              make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                          acc[i][j][4 * g4 + 3]);
+        }
     }
     lds_barrier();
   };
@@ -752,9 +759,9 @@ hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
   static_assert(PipeCfg<BM, BN, BK, S>::kLdsBytes * MINB <= 160 * 1024, "LDS per CU");
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB>),
-                     dim3((unsigned)blocks, (unsigned)splits),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(e),
-                     static_cast<const uint16_t*>(W), M, N, K, ep);
+                     dim3((unsigned)blocks, (unsigned)splits), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), M, N, K,
+                     ep);
   return hipGetLastError();
 }
 
