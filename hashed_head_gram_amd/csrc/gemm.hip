@@ -4,9 +4,11 @@
 // the matrix cores. Both operands are K-contiguous, the layout the MFMA A and
 // B fragments take directly.
 //
-// Main kernel (K a multiple of 64): 256 threads = 4 waves in a 2 x 2 grid,
-// block tile BM x BN (256 x 192 or 256 x 256), wave tile (BM/2) x (BN/2)
-// made of 32 x 32 blocks of v_mfma_f32_32x32x16_bf16 (on gfx950 this form
+// Main kernel (K a multiple of 64): 512 threads = 8 waves, two per SIMD, so
+// one wave's matrix work covers the other's barrier and LDS waits; block
+// tile BM x BN (256 x 192 in a 4 x 2 wave grid, or 256 x 256 in 2 x 4),
+// wave tile 64 x 96 or 128 x 64 made of 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 (on gfx950 this form
 // sustains far more of the bf16 peak than 16 x 16 x 32). K advances 64 at a
 // time through two-buffer LDS rings for the E and W tiles, filled by direct
 // global->LDS loads (global_load_lds_dwordx4: a lane moves 16 bytes, a wave
@@ -178,31 +180,37 @@ struct PipeCfg {
   static constexpr int kRingBytes = S * (kABytes + kBBytes);
   static constexpr int kPad = 4;                 // floats of row padding
   static constexpr int kRowStride = BN + kPad;   // staged accumulator row (floats)
-  // rows of the block tile staged per epilogue pass: as many wave rows
-  // (BM/2) as fit beside nothing else (the ring is dead by then)
+  // rows of the block tile staged per epilogue pass: half the tile if it
+  // fits in the ring's bytes (the ring is dead by then), else a quarter
   static constexpr int kPassRows =
       (BM / 2) * kRowStride * 4 <= kRingBytes ? BM / 2 : BM / 4;
   static constexpr int kStageTileBytes = kPassRows * kRowStride * 4;
   static constexpr int kLdsBytes = kRingBytes > kStageTileBytes ? kRingBytes : kStageTileBytes;
 };
 
-template <int BM, int BN, int BK, int S, int EPI, int MINB>
-__global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
+// WGM x WGN waves (64 WGM WGN threads): 2 x 2 puts one wave on each SIMD;
+// 2 x 4 and 4 x 2 put two, so one wave's matrix work covers the other's
+// barrier and LDS waits.
+template <int BM, int BN, int BK, int S, int EPI, int MINB, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, int64_t M, int N,
     int K, EpiArgs ep) {
   using Cfg = PipeCfg<BM, BN, BK, S>;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int NW = WGM * WGN;                 // waves
+  constexpr int NT = 64 * NW;                   // threads
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA tiles per wave
   constexpr int LPR = BK / 8;                  // 16-byte chunks (lanes) per row
   constexpr int RPI = 64 / LPR;                // rows per DMA instruction
   constexpr int ROWS_PER_LINE = 128 / BK;      // rows per 256-byte LDS line
-  constexpr int A_DMA = BM / RPI / 4;          // DMA instructions per wave per stage
-  constexpr int B_DMA = BN / RPI / 4;
+  constexpr int A_DMA = BM / RPI / NW;         // DMA instructions per wave per stage
+  constexpr int B_DMA = BN / RPI / NW;
   constexpr int L = A_DMA + B_DMA;
   static_assert(BK == 32 || BK == 64, "K stage of 32 or 64");
   static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
   static_assert(2 * L < 64, "vmcnt range");
-  static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile split");
+  static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "tile split");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32 x 32 MFMA tiles per wave");
   static_assert(L < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
   static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   const int64_t nbm = (M + BM - 1) / BM;
   const int64_t nbn = (N + BN - 1) / BN;
@@ -402,8 +410,8 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   constexpr int R = Cfg::kPassRows;
   constexpr int RS = Cfg::kRowStride;
   constexpr int NP = BM / R;                    // passes
-  constexpr int ITEMS = R * CPR / kThreads;     // items per thread per pass
-  static_assert(R * CPR % kThreads == 0, "epilogue items");
+  constexpr int ITEMS = R * CPR / NT;     // items per thread per pass
+  static_assert(R * CPR % NT == 0, "epilogue items");
   auto lds_barrier = [] {
     __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
     asm volatile("" ::: "memory");
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   if (pre_ok && full) {
 #pragma unroll
     for (int q = 0; q < NP * ITEMS; ++q) {
-      const int idx = tid + q * kThreads;
+      const int idx = tid + q * NT;
       pre[q] = *reinterpret_cast<const uint4*>(pre_src + (m0 + idx / CPR) * pre_ld + pre_c0 +
                                                (idx % CPR) * 8);
     }
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   // the thread count), so the gain products are read once.
   float gg[8];
   if constexpr (EPI == EPI_ENGRAM) {
-    static_assert(kThreads % CPR == 0, "every item of a thread has the same columns");
+    static_assert(NT % CPR == 0, "every item of a thread has the same columns");
     const int seg = n0 / ep.d;
     const int c = n0 - seg * ep.d + (tid % CPR) * 8;
 #pragma unroll
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
   };
   // Item it of pass p: tile row rl = (tid + 256 it) / CPR, columns c8..c8+7.
   auto item_y = [&](int p, int it, float (&y)[8], float (&xin)[8]) {
-    const int idx = tid + it * kThreads;
+    const int idx = tid + it * NT;
     const int rl = idx / CPR;
     const int c8 = (idx - rl * CPR) * 8;
     const float4 lo = *reinterpret_cast<const float4*>(&tile[rl * RS + c8]);
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
       stage(p);
 #pragma unroll
       for (int it = 0; it < ITEMS; ++it) {
-        const int idx = tid + it * kThreads;
+        const int idx = tid + it * NT;
         const int64_t row = m0 + p * R + idx / CPR;
         const int col = n0 + (idx % CPR) * 8;
         float y[8], xin[8];
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
         uint16_t* obase = ep.out + (m0 + p * R) * (int64_t)N + n0;
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-          const int idx = tid + it * kThreads;
+          const int idx = tid + it * NT;
           const uint32_t off = (uint32_t)((idx / CPR) * N + (idx % CPR) * 8);
           float y[8], xin[8];
           item_y(p, it, y, xin);
@@ -526,7 +534,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
         stage(p);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-          const int idx = tid + it * kThreads;
+          const int idx = tid + it * NT;
           const int64_t row = m0 + p * R + idx / CPR;
           const int col = n0 + (idx % CPR) * 8;
           float y[8], xin[8];
@@ -550,7 +558,7 @@ __global__ __launch_bounds__(kThreads, MINB) void gemm_bf16_pipe_kernel(
       stage(p);
 #pragma unroll
       for (int it = 0; it < ITEMS; ++it) {
-        const int idx = tid + it * kThreads;
+        const int idx = tid + it * NT;
         const int c8 = (idx % CPR) * 8;
         const int64_t row = m0 + p * R + idx / CPR;
         const int c = n0 + c8 - seg * ep.d;
@@ -752,14 +760,15 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
   }
 }
 
-// BM x BN tiles, K stages of BK through a ring of S, MINB blocks per CU.
-template <int BM, int BN, int BK, int S, int MINB, int EPI>
+// BM x BN tiles, K stages of BK through a ring of S, MINB blocks per CU,
+// WGM x WGN waves per block.
+template <int BM, int BN, int BK, int S, int MINB, int EPI, int WGM = 2, int WGN = 2>
 hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
                        const EpiArgs& ep, hipStream_t s, int splits = 1) {
   static_assert(PipeCfg<BM, BN, BK, S>::kLdsBytes * MINB <= 160 * 1024, "LDS per CU");
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB>),
-                     dim3((unsigned)blocks, (unsigned)splits), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB, WGM, WGN>),
+                     dim3((unsigned)blocks, (unsigned)splits), dim3(64 * WGM * WGN), 0, s,
                      static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), M, N, K,
                      ep);
   return hipGetLastError();
@@ -788,8 +797,8 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
       return ((blocks + 255) / 256) * bn;
     };
     if (cost(192) < cost(256))
-      return launch_pipe<256, 192, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
-    return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_SCALAR>(e, N, (int)d, (int)E, W, ep, s);
+      return launch_pipe<256, 192, kPipeBK, kPipeStages, 1, EPI_SCALAR, 4, 2>(e, N, (int)d, (int)E, W, ep, s);
+    return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_SCALAR, 2, 4>(e, N, (int)d, (int)E, W, ep, s);
   }
   constexpr int BM = 128, BN = 128;
   const int64_t blocks = ((N + BM - 1) / BM) * ((d + BN - 1) / BN);
@@ -811,7 +820,7 @@ hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64
   ep.ldo = ldo;
   ep.lda = lda;
   ep.ldb = ldb;
-  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_F32>(A, M, N, Kc, B, ep, s, splits);
+  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_F32, 2, 4>(A, M, N, Kc, B, ep, s, splits);
 }
 
 // Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller).
@@ -828,7 +837,7 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
-  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM>(e, N, (int)((1 + Mbr) * d),
+  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM, 2, 4>(e, N, (int)((1 + Mbr) * d),
                                                                    (int)E, W, ep, s);
 }
 
