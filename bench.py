@@ -18,6 +18,11 @@ Prints one JSON line: whole-job tokens/s, the roofline position of the
 dominant kernel (algorithmic bytes or flops per launch over its mean launch
 duration), both kernels' figures, and the CPU oracle timed on a bounded
 sample on the host cores.
+
+--fp8 times the same path with E4M3 projection operands instead
+(pg_forward_fp8 = pg_index_gather_fp8 + pg_project_gate_fp8; W quantised
+once before timing): a separate line at another precision, never the
+headline.
 """
 import argparse
 import hashlib
@@ -31,9 +36,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 POOL = 32
 DEFAULT_WORKLOAD = "pagegram200m_bf16_8x2048"
+# E4M3 scale exponents of the --fp8 mode: e ~ N(0, 0.02) rows (NF4: |e| <=
+# about 0.05) and W ~ N(0, 0.05) times 2^s stay well below 448
+FP8_E_SCALE = {"bf16": 11, "nf4": 13, "f32": 11}
+FP8_W_SCALE = 10
 
 
 def parse():
@@ -53,30 +63,34 @@ def parse():
                    help="flash page-cache figures (reads/token under an LRU RAM cache) "
                         "of the 20B NF4 table in the PageGram S=4, S=15 and Engram-style "
                         "layouts, from pg_index rows of the token pool")
+    p.add_argument("--fp8", action="store_true",
+                   help="E4M3 projection operands (pg_forward_fp8); a separate line")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 --pmc counter "
                         "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run")
     return p.parse_args()
 
 
-def algorithmic_costs(wl):
+def algorithmic_costs(wl, fp8=False):
     """Per-token algorithmic HBM bytes of index+gather and flops/bytes of the
-    projection stage (the figures the roofline uses)."""
+    projection stage (the figures the roofline uses). fp8: e is one byte per
+    element (residual and output stay bf16)."""
     lay = wl["layout"]
     O = lay["n_max"] - lay["n_min"] + 1
     K, r = lay["K"], lay["r"]
     elt = 4 if wl["act_dtype"] == "f32" else 2
+    e_elt = 1 if fp8 else elt
     row_bytes = {"f32": 4 * r, "bf16": 2 * r, "nf4": r // 2 + 2}[wl["table_dtype"]]
     E = O * K * r
-    gather_bytes = 4 + O * K * row_bytes + E * elt
+    gather_bytes = 4 + O * K * row_bytes + E * e_elt
     if wl["gate"] == "engram":
         M, d = wl["M"], wl["d"]
         flops = 2 * E * (1 + M) * d
-        proj_bytes = E * elt + 2 * M * d * elt   # e in; h in, out (pass 1 + 2 read h)
+        proj_bytes = E * e_elt + 2 * M * d * elt   # e in; h in, out (pass 1 + 2 read h)
     else:
         d = wl["d"]
         flops = 2 * E * d
-        proj_bytes = E * elt + 2 * d * elt       # e in; x in, out
+        proj_bytes = E * e_elt + 2 * d * elt       # e in; x in, out
     return dict(gather_bytes=gather_bytes, proj_flops=flops, proj_bytes=proj_bytes, E=E)
 
 
@@ -109,7 +123,7 @@ def traffic_for(stage, workload):
 
 
 COPY_BYTES = 1 << 30
-TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_bf16_pipe_kernel",
+TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_kernel",
                    "copy": "copyBuffer"}
 
 
@@ -402,8 +416,12 @@ def main():
     r = lay_d["r"]
     B, T = wl["B"], wl["T"]
     N = B * T
-    costs = algorithmic_costs(wl)
+    fp8 = args.fp8
+    costs = algorithmic_costs(wl, fp8)
     E = costs["E"]
+    if fp8 and (wl["act_dtype"] != "bf16" or E % 128):
+        sys.exit(f"--fp8 needs bf16 activations and an e dimension that is a multiple of "
+                 f"128 ({wl['name']}: {wl['act_dtype']}, {E})")
     act = torch.float32 if wl["act_dtype"] == "f32" else torch.bfloat16
     e_dtype = pg.PG_F32 if wl["act_dtype"] == "f32" else pg.PG_BF16
 
@@ -440,19 +458,41 @@ def main():
     sdev.fill_normal(resid, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
     ws = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8, device=dev)
     # pg_forward's constituents, for per-kernel timing.
-    e = torch.empty(N, E, dtype=act, device=dev)
+    e = torch.empty(N, E, dtype=torch.uint8 if fp8 else act, device=dev)
     ws2 = torch.empty_like(ws)
-    torch.cuda.synchronize()
+    if fp8:
+        # E4M3 scale exponents: |e| 2^se and |W| 2^sw stay well below 448
+        se = FP8_E_SCALE[wl["table_dtype"]]
+        sw = FP8_W_SCALE
+        W8 = torch.empty(d_out, E, dtype=torch.uint8, device=dev)
+        pg.pg_quantize_fp8(W, pg.PG_BF16, sw, W8)
 
-    def forward(j):
-        pg.pg_forward(layout, table, fuse, pool[j % POOL], cmap, W, resid, out, ws)
+        def forward(j):
+            pg.pg_forward_fp8(layout, table, fuse, pool[j % POOL], cmap, W8, se, sw, resid,
+                              out, ws)
+
+        def gather_call(j):
+            pg.pg_index_gather_fp8(layout, table, pool[j % POOL], cmap, se, e)
+
+        def project_call(j):
+            pg.pg_project_gate_fp8(fuse, e, B, T, W8, se, sw, resid, out, ws2)
+    else:
+        def forward(j):
+            pg.pg_forward(layout, table, fuse, pool[j % POOL], cmap, W, resid, out, ws)
+
+        def gather_call(j):
+            pg.pg_index_gather(layout, table, pool[j % POOL], cmap, e_dtype, e)
+
+        def project_call(j):
+            pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws2)
+    torch.cuda.synchronize()
 
     # The stage calls reproduce pg_forward bit for bit.
     out_fwd = torch.empty_like(out)
     forward(0)
     out_fwd.copy_(out)
-    pg.pg_index_gather(layout, table, pool[0], cmap, e_dtype, e)
-    pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws2)
+    gather_call(0)
+    project_call(0)
     torch.cuda.synchronize()
     same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
     del out_fwd
@@ -482,10 +522,8 @@ def main():
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps
-    g_ms = np.array([per_launch_ms(lambda j: pg.pg_index_gather(
-        layout, table, pool[j % POOL], cmap, e_dtype, e))])
-    p_ms = np.array([per_launch_ms(lambda j: pg.pg_project_gate(
-        fuse, e, B, T, W, resid, out, ws2))])
+    g_ms = np.array([per_launch_ms(gather_call)])
+    p_ms = np.array([per_launch_ms(project_call)])
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -500,21 +538,24 @@ def main():
     p_flops = costs["proj_flops"] * N
     p_bytes = costs["proj_bytes"] * N
     g_gbps = g_bytes / (g_ms.mean() / 1e3) / 1e9
-    p_peak = FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS
+    p_peak = (FP8_PEAK_TFLOPS if fp8 else
+              FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS)
+    tkey = wl["name"] + ("/fp8" if fp8 else "")
     p_tflops = p_flops / (p_ms.mean() / 1e3) / 1e12
     gather_rec = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
                   "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
                   "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
-                  "traffic": traffic_for("gather", wl["name"])}
-    proj = {"kernel": ("gemm_bf16_pipe_kernel" if E % 32 == 0 else "gemm_bf16_kernel")
+                  "traffic": traffic_for("gather", tkey)}
+    proj = {"kernel": ("gemm_pipe_kernel" if E % (128 if fp8 else 64) == 0 else "gemm_bf16_kernel")
             if act == torch.bfloat16 else "gemm_f32_kernel",
             "ms_mean": float(p_ms.mean()), "flops_per_launch": p_flops,
             "achieved_TFLOPs": p_tflops, "frac_mfma_peak": p_tflops / p_peak,
             "bytes_per_launch": p_bytes,
             "achieved_GBps": p_bytes / (p_ms.mean() / 1e3) / 1e9,
-            "traffic": traffic_for("projection", wl["name"])}
-    stages = {"pg_index_gather_ms": float(g_ms.mean()),
-              "pg_project_gate_ms": float(p_ms.mean())}
+            "traffic": traffic_for("projection", tkey)}
+    sfx = "_fp8" if fp8 else ""
+    stages = {f"pg_index_gather{sfx}_ms": float(g_ms.mean()),
+              f"pg_project_gate{sfx}_ms": float(p_ms.mean())}
     if g_ms.mean() >= p_ms.mean():
         roof = {"kernel": gather_rec["kernel"], "bound": "hbm", "achieved": g_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
@@ -524,13 +565,15 @@ def main():
                 "peak": p_peak, "unit": "TFLOP/s", "frac": p_tflops / p_peak,
                 "traffic": proj["traffic"]}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         cpu = cpu_baseline(wl, args.cpu_tokens)
     line = {
-        "metric": "M tokens/s for hash+gather+project; gather HBM GB/s and % of peak",
+        "metric": "M tokens/s for hash+gather+project; gather HBM GB/s and % of peak"
+                  + (" (FP8 E4M3 projection operands)" if fp8 else ""),
         "value": tok_s / 1e6, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl["act_dtype"],
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 operands, fp32 accumulate, bf16 out" if fp8 else wl["act_dtype"],
         "data": "synthetic (seeded Zipf token streams, counter-generated table and weights)",
         "config": {"workload": wl["name"], "tokens_per_step": N, "batch": B, "seq_len": T,
                    "layout": lay_d["kind"], "K": lay_d["K"], "S": lay_d["S"], "r": r,

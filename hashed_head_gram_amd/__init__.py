@@ -57,6 +57,13 @@ _SIGS = {
                                _vp, _i64, _vp]),
     "pg_forward": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                           _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pg_quantize_fp8": (_i32, [_vp, _i32, _i64, _i32, _vp, _vp]),
+    "pg_index_gather_fp8": (_i32, [_P(PgLayout), _P(PgTable), _vp, _i64, _i64, _vp,
+                                   _i64, _i32, _vp, _vp, _vp]),
+    "pg_project_gate_fp8": (_i32, [_P(PgFuse), _vp, _i64, _i64, _i64, _vp, _i32, _i32,
+                                   _vp, _vp, _vp, _i64, _vp]),
+    "pg_forward_fp8": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
+                              _vp, _i64, _vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _vp]),
     "pg_strerror": (ctypes.c_char_p, [_i32]),
     "pg_hash_version": (ctypes.c_uint32, []),
     "pg_layout_rows": (_i32, [_P(PgLayout), _P(_i64)]),
@@ -223,6 +230,45 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) operands
+
+
+def pg_quantize_fp8(src, src_dtype, scale_exp, dst, stream=None):
+    """dst (uint8, same element count) = E4M3(src * 2^scale_exp)."""
+    _check("pg_quantize_fp8", lib().pg_quantize_fp8(
+        _ptr(src), src_dtype, src.numel(), int(scale_exp), _ptr(dst), _stream(stream)))
+
+
+def pg_index_gather_fp8(layout, table, tokens, canon_map, e_scale_exp, e_out,
+                        dev_status=None, stream=None):
+    B, T = tokens.shape
+    _check("pg_index_gather_fp8", lib().pg_index_gather_fp8(
+        ctypes.byref(layout), ctypes.byref(table), _ptr(tokens), B, T,
+        _ptr(canon_map), canon_map.numel(), int(e_scale_exp), _ptr(e_out),
+        _ptr(dev_status), _stream(stream)))
+
+
+def pg_project_gate_fp8(fuse, e8, B, T, W8, e_scale_exp, w_scale_exp, resid, out,
+                        workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pg_project_gate_fp8", lib().pg_project_gate_fp8(
+        ctypes.byref(fuse), _ptr(e8), int(B), int(T), e8.shape[-1], _ptr(W8),
+        int(e_scale_exp), int(w_scale_exp), _ptr(resid), _ptr(out), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def pg_forward_fp8(layout, table, fuse, tokens, canon_map, W8, e_scale_exp, w_scale_exp,
+                   resid, out, workspace, dev_status=None, stream=None):
+    B, T = tokens.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pg_forward_fp8", lib().pg_forward_fp8(
+        ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
+        B, T, _ptr(canon_map), canon_map.numel(), _ptr(W8), int(e_scale_exp),
+        int(w_scale_exp), _ptr(resid), _ptr(out), _ptr(workspace), ws_bytes,
+        _ptr(dev_status), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -4,13 +4,6 @@
 
 #include "common.h"
 
-namespace pg {
-hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
-                               int64_t d, int64_t Mbr, const void* h,
-                               const float* gamma_h, const float* gamma_k, uint16_t* v,
-                               float* part_v, float* part_k, hipStream_t s);
-}
-
 namespace {
 
 using pg::DevLayout;
@@ -153,7 +146,37 @@ int run_project(const pg_fuse* f, const void* e, int64_t B, int64_t T, int64_t e
   return hip_status(pg::launch_engram(e, B, T, e_dim, W, f->d, f->M, f->eps, f->gamma_h,
                                       f->gamma_k, f->gamma_u, f->conv_w, f->conv_k,
                                       f->conv_dil, resid, out, ws, f->increment_only ? 0 : 1,
-                                      s));
+                                      0, 0, 0, s));
+}
+
+// FP8 operands: scale exponents within +-64, e_dim a multiple of 128 (the
+// FP8 MFMA's K stage), bf16 residual and output.
+constexpr int kMaxScaleExp = 64;
+bool scale_ok(int32_t se) { return se >= -kMaxScaleExp && se <= kMaxScaleExp; }
+
+int check_fp8_fuse(const pg_fuse* f, int64_t B, int64_t T, int64_t e_dim, int32_t se,
+                   int32_t sw) {
+  const int st = check_fuse(f, B, T, e_dim);
+  if (st != PG_OK) return st;
+  if (!scale_ok(se) || !scale_ok(sw)) return PG_EINVAL;
+  if (f->dtype != PG_BF16) return PG_EUNSUPPORTED;
+  if (e_dim % 128) return PG_EUNSUPPORTED;
+  return PG_OK;
+}
+
+int run_project_fp8(const pg_fuse* f, const void* e8, int64_t B, int64_t T, int64_t e_dim,
+                    const void* W8, int32_t se, int32_t sw, const void* resid, void* out,
+                    void* ws, hipStream_t s) {
+  const int64_t N = B * T;
+  if (f->gate == PG_GATE_SCALAR) {
+    const void* x = f->increment_only ? nullptr : resid;
+    return hip_status(
+        pg::launch_project_scalar_fp8(e8, N, e_dim, W8, f->d, f->g, x, out, se, sw, s));
+  }
+  return hip_status(pg::launch_engram(e8, B, T, e_dim, W8, f->d, f->M, f->eps, f->gamma_h,
+                                      f->gamma_k, f->gamma_u, f->conv_w, f->conv_k,
+                                      f->conv_dil, resid, out, ws, f->increment_only ? 0 : 1,
+                                      1, se, sw, s));
 }
 
 }  // namespace
@@ -248,7 +271,7 @@ PG_API int pg_index_gather(const pg_layout* layout, const pg_table* table,
   if (B * T == 0) return PG_OK;
   if (!e_out || !aligned(e_out, 16)) return PG_EINVAL;
   return hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales,
-                                            tokens, B, T, canon_map, V, e_out, dev_status,
+                                            tokens, B, T, canon_map, V, e_out, dev_status, 0, 0,
                                             stream));
 }
 
@@ -296,9 +319,92 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
   void* e = workspace;
   void* ws = static_cast<uint8_t*>(workspace) + e_bytes;
   st = hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales, tokens,
-                                          B, T, canon_map, V, e, dev_status, stream));
+                                          B, T, canon_map, V, e, dev_status, 0, 0, stream));
   if (st != PG_OK) return st;
   return run_project(fuse, e, B, T, e_dim, W, resid, out, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) operands
+
+PG_API int pg_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, int32_t scale_exp,
+                           uint8_t* dst, hipStream_t stream) {
+  if (n < 0 || !scale_ok(scale_exp)) return PG_EINVAL;
+  if (src_dtype != PG_BF16 && src_dtype != PG_F32) return PG_EINVAL;
+  if (n == 0) return PG_OK;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_quantize_fp8(src, src_dtype, n, scale_exp, dst, stream));
+}
+
+PG_API int pg_index_gather_fp8(const pg_layout* layout, const pg_table* table,
+                               const int32_t* tokens, int64_t B, int64_t T,
+                               const int32_t* canon_map, int64_t V, int32_t e_scale_exp,
+                               uint8_t* e_out, int32_t* dev_status, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  if (!scale_ok(e_scale_exp)) return PG_EINVAL;
+  if (B * T == 0) return PG_OK;
+  if (!e_out || !aligned(e_out, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales,
+                                            tokens, B, T, canon_map, V, e_out, dev_status, 1,
+                                            e_scale_exp, stream));
+}
+
+PG_API int pg_project_gate_fp8(const pg_fuse* fuse, const uint8_t* e8, int64_t B, int64_t T,
+                               int64_t e_dim, const uint8_t* W8, int32_t e_scale_exp,
+                               int32_t w_scale_exp, const void* resid, void* out,
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  int st = check_fp8_fuse(fuse, B, T, e_dim, e_scale_exp, w_scale_exp);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!e8 || !W8 || !out) return PG_EINVAL;
+  if (!aligned(e8, 16) || !aligned(W8, 16) || !aligned(out, 16)) return PG_EINVAL;
+  if (resid && !aligned(resid, 16)) return PG_EINVAL;
+  if (fuse->gate == PG_GATE_ENGRAM && !resid) return PG_EINVAL;
+  const int64_t need = project_workspace(fuse, N);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PG_EINVAL;
+  return run_project_fp8(fuse, e8, B, T, e_dim, W8, e_scale_exp, w_scale_exp, resid, out,
+                         workspace, stream);
+}
+
+PG_API int pg_forward_fp8(const pg_layout* layout, const pg_table* table, const pg_fuse* fuse,
+                          const int32_t* tokens, int64_t B, int64_t T, const int32_t* canon_map,
+                          int64_t V, const uint8_t* W8, int32_t e_scale_exp,
+                          int32_t w_scale_exp, const void* resid, void* out, void* workspace,
+                          int64_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  const int64_t e_dim = (int64_t)L.O * L.K * L.r;
+  st = check_fp8_fuse(fuse, B, T, e_dim, e_scale_exp, w_scale_exp);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!W8 || !out || !aligned(W8, 16) || !aligned(out, 16)) return PG_EINVAL;
+  if (resid && !aligned(resid, 16)) return PG_EINVAL;
+  if (fuse->gate == PG_GATE_ENGRAM && !resid) return PG_EINVAL;
+  const int64_t e_bytes = align256(N * e_dim);
+  const int64_t need = e_bytes + project_workspace(fuse, N);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PG_EINVAL;
+  auto* e8 = static_cast<uint8_t*>(workspace);
+  void* ws = e8 + e_bytes;
+  st = hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales, tokens,
+                                          B, T, canon_map, V, e8, dev_status, 1, e_scale_exp,
+                                          stream));
+  if (st != PG_OK) return st;
+  return run_project_fp8(fuse, e8, B, T, e_dim, W8, e_scale_exp, w_scale_exp, resid, out, ws,
+                         stream);
 }
 
 // ---------------------------------------------------------------------------

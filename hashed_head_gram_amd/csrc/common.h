@@ -146,6 +146,29 @@ __device__ __forceinline__ uint64_t sign_word(const DevLayout& L, const uint64_t
 // ---------------------------------------------------------------------------
 // Float helpers
 
+// fp32 -> OCP E4M3 (sign, 4-bit exponent of bias 7, 3-bit mantissa; no
+// infinities; 0x7F / 0xFF NaN; largest finite 448): round to nearest, ties
+// to the even mantissa, magnitudes >= 448 saturate to 448, NaN stays NaN,
+// the sign of zero is kept. Integer arithmetic on the fp32 bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448, infinities
+  if (a < 0x3C800000u) {                             // |x| < 2^-6: subnormal codes
+    // q = |x| 2^9 rounded to nearest even (exact scaling); q = 8 is the
+    // smallest normal, code 0x08
+    const uint32_t q = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | q;
+  }
+  // normal: bits 30..20 hold (exponent << 3 | top 3 mantissa bits); round
+  // to nearest even at bit 20, then rebias the exponent from 127 to 7
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  const uint32_t code = r - (120u << 3);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
@@ -169,15 +192,25 @@ hipError_t launch_gather(const DevLayout& L, int32_t table_dtype, const void* ta
                          const void* scales, const int64_t* rows, const uint64_t* signs,
                          int64_t n_tok, void* e_out, hipStream_t s);
 
+// e_fp8: write e as E4M3(e 2^e_scale_exp) bytes instead of bf16 / fp32.
 hipError_t launch_index_gather(const DevLayout& L, int32_t table_dtype, const void* table,
                                const void* scales, const int32_t* tokens, int64_t B,
                                int64_t T, const int32_t* cmap, int64_t V, void* e_out,
-                               int32_t* status, hipStream_t s);
+                               int32_t* status, int e_fp8, int e_scale_exp, hipStream_t s);
+
+// dst[i] = E4M3(src[i] 2^scale_exp) for bf16 or fp32 src.
+hipError_t launch_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, int scale_exp,
+                               uint8_t* dst, hipStream_t s);
 
 // Scalar-gate projection: out[N][d] = resid + g * e W^T.
 hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_t E,
                                  const void* W, int64_t d, float g, const void* resid,
                                  void* out, hipStream_t s);
+
+// The same on E4M3 operands e8 = E4M3(e 2^se), W8 = E4M3(W 2^sw).
+hipError_t launch_project_scalar_fp8(const void* e8, int64_t N, int64_t E, const void* W8,
+                                     int64_t d, float g, const void* resid, void* out,
+                                     int se, int sw, hipStream_t s);
 
 // fp32-output GEMM with optional split K (partials at out + s * M * ldo).
 hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64_t M, int N,
@@ -209,12 +242,19 @@ hipError_t launch_rms_step(const int64_t* urows, const float* ugrad, const int64
 hipError_t launch_rms_flush(int64_t R, int r, float* table, float* vhat, int64_t* last,
                             int64_t step, float lr, float beta2, float wd, hipStream_t s);
 
-// Engram fusion (bf16): workspace layout described in engram_workspace_bytes.
+// Engram fusion (bf16 or, with f8, E4M3 operands of scales se, sw): workspace
+// layout described in engram_workspace_bytes.
 int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M);
+hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
+                               int64_t d, int64_t Mbr, const void* h,
+                               const float* gamma_h, const float* gamma_k, uint16_t* v,
+                               float* part_v, float* part_k, int f8, int se, int sw,
+                               hipStream_t s);
 hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
                          int64_t d, int64_t M, float eps, const float* gamma_h,
                          const float* gamma_k, const float* gamma_u, const float* conv_w,
                          int conv_k, int conv_dil, const void* h, void* out,
-                         void* workspace, int add_resid, hipStream_t s);
+                         void* workspace, int add_resid, int f8, int se, int sw,
+                         hipStream_t s);
 
 }  // namespace pg

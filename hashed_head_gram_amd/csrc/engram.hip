@@ -20,11 +20,6 @@
 
 namespace pg {
 
-hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
-                               int64_t d, int64_t Mbr, const void* h,
-                               const float* gamma_h, const float* gamma_k, uint16_t* v,
-                               float* part_v, float* part_k, hipStream_t s);
-
 namespace {
 
 constexpr int kThreads = 256;
@@ -184,7 +179,8 @@ hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const v
                          int64_t d, int64_t M, float eps, const float* gamma_h,
                          const float* gamma_k, const float* gamma_u, const float* conv_w,
                          int conv_k, int conv_dil, const void* h, void* out,
-                         void* workspace, int add_resid, hipStream_t s) {
+                         void* workspace, int add_resid, int f8, int se, int sw,
+                         hipStream_t s) {
   const int64_t N = B * T;
   const int64_t n_cb = d / kColBlock;
   auto* base = static_cast<uint8_t*>(workspace);
@@ -194,7 +190,7 @@ hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const v
   auto* gate = reinterpret_cast<float*>(base + align256(N * d * 2) + align256(n_cb * N * 4) +
                                         align256(M * 3 * n_cb * N * 4));
   hipError_t err = launch_engram_pass1(e, N, E, W, d, M, h, gamma_h, gamma_k, v, part_v,
-                                       part_k, s);
+                                       part_k, f8, se, sw, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(engram_gate_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads),
                                               (unsigned)M),

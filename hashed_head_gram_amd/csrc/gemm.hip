@@ -44,12 +44,15 @@
 // staged double buffer; scalar gate only.
 //
 // fp32: a plain LDS-tiled FMA GEMM for fp32 tables (tiny workloads).
+#include <type_traits>
+
 #include "common.h"
 
 namespace pg {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));   // 32 FP8 values
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -57,7 +60,8 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kColBlock = 256;   // Engram partial-sum column block
-constexpr int kPipeBK = 64;      // K stage of the pipelined kernel
+constexpr int kPipeBK = 64;      // K stage of the pipelined kernel (bf16 elements)
+constexpr int kPipeBK8 = 128;    // the same 128 bytes per row in FP8 elements
 constexpr int kPipeStages = 2;   // its LDS ring
 
 enum { EPI_SCALAR = 0, EPI_ENGRAM = 1, EPI_F32 = 2 };
@@ -83,6 +87,9 @@ struct EpiArgs {
   int64_t ldo;
   // operand row strides in elements (0: K)
   int lda, ldb;
+  // FP8 operands: E8M0 scales of the MFMA's A (W) and B (e) operands,
+  // 127 - s for an operand stored as E4M3(v 2^s)
+  int f8_sa, f8_sb;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -170,12 +177,13 @@ __device__ __forceinline__ void epi_scalar(const f32x4_t (&acc)[FM][FN], int64_t
 // ---------------------------------------------------------------------------
 // Pipelined kernel
 
-// LDS bytes of the K ring and of the epilogue's staging tile.
-template <int BM, int BN, int BK, int S>
+// LDS bytes of the K ring and of the epilogue's staging tile; BKB is the
+// bytes of one row's K stage.
+template <int BM, int BN, int BKB, int S>
 struct PipeCfg {
   // rings of S buffers for the E and the W tiles (S - 1 stages in flight)
-  static constexpr int kABytes = BM * BK * 2;
-  static constexpr int kBBytes = BN * BK * 2;
+  static constexpr int kABytes = BM * BKB;
+  static constexpr int kBBytes = BN * BKB;
   static constexpr int kBOffset = S * kABytes;
   static constexpr int kRingBytes = S * (kABytes + kBBytes);
   static constexpr int kPad = 4;                 // floats of row padding
@@ -190,23 +198,28 @@ struct PipeCfg {
 
 // WGM x WGN waves (64 WGM WGN threads): 2 x 2 puts one wave on each SIMD;
 // 2 x 4 and 4 x 2 put two, so one wave's matrix work covers the other's
-// barrier and LDS waits.
-template <int BM, int BN, int BK, int S, int EPI, int MINB, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, int64_t M, int N,
+// barrier and LDS waits. F8: E4M3 operands (BK = 128 K elements per stage)
+// on v_mfma_scale_f32_32x32x64_f8f6f4, whose E8M0 operand scales undo the
+// operands' power-of-two scaling; otherwise bf16 (BK = 64) on
+// v_mfma_f32_32x32x16_bf16. Either way a row's K stage is 128 bytes.
+template <int BM, int BN, int BK, int S, int EPI, int MINB, int WGM, int WGN, bool F8>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bw, int64_t M, int N,
     int K, EpiArgs ep) {
-  using Cfg = PipeCfg<BM, BN, BK, S>;
+  constexpr int EB = F8 ? 1 : 2;                // operand element bytes
+  constexpr int BKB = BK * EB;                  // bytes of a row's K stage
+  using Cfg = PipeCfg<BM, BN, BKB, S>;
   constexpr int NW = WGM * WGN;                 // waves
   constexpr int NT = 64 * NW;                   // threads
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA tiles per wave
-  constexpr int LPR = BK / 8;                  // 16-byte chunks (lanes) per row
+  constexpr int LPR = BKB / 16;                // 16-byte chunks (lanes) per row
   constexpr int RPI = 64 / LPR;                // rows per DMA instruction
-  constexpr int ROWS_PER_LINE = 128 / BK;      // rows per 256-byte LDS line
+  constexpr int ROWS_PER_LINE = 256 / BKB;     // rows per 256-byte LDS line
   constexpr int A_DMA = BM / RPI / NW;         // DMA instructions per wave per stage
   constexpr int B_DMA = BN / RPI / NW;
   constexpr int L = A_DMA + B_DMA;
-  static_assert(BK == 32 || BK == 64, "K stage of 32 or 64");
+  static_assert(BKB == 64 || BKB == 128, "K stage of 64 or 128 bytes");
   static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
   static_assert(2 * L < 64, "vmcnt range");
   static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "tile split");
@@ -220,8 +233,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
   const int64_t lda = ep.lda ? ep.lda : K;
   const int64_t ldb = ep.ldb ? ep.ldb : K;
   if constexpr (EPI == EPI_F32) {
-    A += (int64_t)blockIdx.y * K;
-    Bw += (int64_t)blockIdx.y * K;
+    A += (int64_t)blockIdx.y * K * EB;
+    Bw += (int64_t)blockIdx.y * K * EB;
   }
 
   const int tid = threadIdx.x;
@@ -282,13 +295,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
   // fixed by the group index.
   const uint32_t chunk_b = (uint32_t)((dpos ^ swz(dr)) * 16);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_rows = [&](const uint16_t* mat, int64_t ld, int64_t rows, int64_t r0, int grp,
+  auto issue_rows = [&](const uint8_t* mat, int64_t ld, int64_t rows, int64_t r0, int grp,
                         int kt, uint32_t lds) {
     int64_t rb = r0 < rows ? r0 : rows - 1;
     const int lim = (int)(rows - 1 - rb);
     const int rr = dr < lim ? dr : lim;
-    dma16(mat + rb * ld + kt * BK,
-          (uint32_t)(rr * ld * 2) + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)), lds);
+    dma16(mat + (rb * ld + (int64_t)kt * BK) * EB,
+          (uint32_t)(rr * ld * EB) + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)), lds);
   };
   auto issue_a = [&](int kt) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
@@ -319,27 +332,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
   // tile: lane l holds token row l % 32 and, per q / 4, the four consecutive
   // output columns 8 (q / 4) + 4 (l / 32) + 0..3 -- contiguous in memory.
   const int fr = lane & 31;
-  // Fragments of K step s (16 wide, s = 0..3) of stage kt: logical 16-byte
-  // chunk 2 s + lane / 32 of row fr of each 32-row tile, stored at that
-  // chunk ^ swz(row).
-  auto load_frags = [&](int kt, int st, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
-    const uint16_t* sa = reinterpret_cast<const uint16_t*>(smem + (kt % S) * Cfg::kABytes);
-    const uint16_t* sb =
-        reinterpret_cast<const uint16_t*>(smem + Cfg::kBOffset + (kt % S) * Cfg::kBBytes);
-    const int pos = ((st * 2 + (lane >> 5)) ^ swz(fr)) * 8;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[(wm * WTM + i * 32 + fr) * BK + pos]));
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sb[(wn * WTN + j * 32 + fr) * BK + pos]));
+  // K steps per stage and their operand type: bf16 steps are 16 wide (one
+  // 16-byte chunk per lane: logical chunk 2 s + lane / 32 of the row), FP8
+  // steps 64 wide (two chunks per lane: 4 s + 2 (lane / 32) and the next);
+  // a chunk sits at its logical index ^ swz(row).
+  constexpr int KSTEP = F8 ? 64 : 16;
+  constexpr int NS = BK / KSTEP;
+  constexpr int CPF = F8 ? 2 : 1;               // 16-byte LDS reads per fragment
+  using frag_t = typename std::conditional<F8, i32x8_t, bf16x8_t>::type;
+  auto read_frag = [&](const uint8_t* rowp, int st) -> frag_t {
+    if constexpr (F8) {
+      const int c0 = 4 * st + 2 * (lane >> 5);
+      const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((c0 ^ swz(fr)) * 16));
+      const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((c0 + 1) ^ swz(fr)) * 16));
+      return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const int c = (st * 2 + (lane >> 5)) ^ swz(fr);
+      return as_bf16x8(*reinterpret_cast<const uint4*>(rowp + c * 16));
+    }
   };
-  auto mma = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bf)[FN]) {
+  auto load_frags = [&](int kt, int st, frag_t (&af)[FM], frag_t (&bf)[FN]) {
+    const uint8_t* sa = smem + (kt % S) * Cfg::kABytes;
+    const uint8_t* sb = smem + Cfg::kBOffset + (kt % S) * Cfg::kBBytes;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = read_frag(sa + (wm * WTM + i * 32 + fr) * BKB, st);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[j] = read_frag(sb + (wn * WTN + j * 32 + fr) * BKB, st);
+  };
+  auto mma = [&](const frag_t (&af)[FM], const frag_t (&bf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bf[j], af[i], acc[i][j], 0, 0, 0, ep.f8_sa, 0, ep.f8_sb);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      }
   };
   auto block_sync = [] {
     asm volatile("" ::: "memory");
@@ -354,9 +385,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
   // after each MFMA of step st (LDS latency hides behind issued matrix work).
   const int KT = K / BK;
   constexpr int PD = S - 1;                     // stages in flight
-  constexpr int NS = BK / 16;                   // K steps per stage
-  constexpr int RD = FM + FN;                   // fragment reads per step
-  static_assert(FM * FN >= RD, "reads interleave with the step's MFMAs");
+  constexpr int RD = (FM + FN) * CPF;           // LDS reads per step
+  constexpr int NMF = FM * FN;                  // MFMAs per step
+  constexpr int RPM = (RD + NMF - 1) / NMF;     // reads issued after each MFMA
 #pragma unroll
   for (int st = 0; st < PD; ++st)
     if (st < KT) {
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
       issue_b(kt + PD);
       issue_a(kt + PD);
     }
-    bf16x8_t fa[NS][FM], fb[NS][FN];
+    frag_t fa[NS][FM], fb[NS][FN];
     load_frags(kt, 0, fa[0], fb[0]);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -388,14 +419,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_pipe_kernel(
       mma(fa[st], fb[st]);
       if (st == 0) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
       if (st + 1 < NS) {
+        // RPM reads after each MFMA until the step's RD reads are out
+        constexpr int FULL = RD / RPM;          // MFMAs followed by RPM reads
+        constexpr int REM = RD - FULL * RPM;    // reads after MFMA FULL
 #pragma unroll
-        for (int q = 0; q < RD; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        for (int q = 0; q < FULL; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);   // RPM LDS reads
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - RD, 0);
+        if constexpr (REM > 0) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, REM, 0);
+        }
+        constexpr int REST = NMF - FULL - (REM > 0 ? 1 : 0);
+        if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
       }
     }
   }
@@ -760,16 +799,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
   }
 }
 
-// BM x BN tiles, K stages of BK through a ring of S, MINB blocks per CU,
-// WGM x WGN waves per block.
-template <int BM, int BN, int BK, int S, int MINB, int EPI, int WGM = 2, int WGN = 2>
+// BM x BN tiles, K stages of BK elements through a ring of S, MINB blocks
+// per CU, WGM x WGN waves per block; F8: E4M3 operands.
+template <int BM, int BN, int BK, int S, int MINB, int EPI, int WGM = 2, int WGN = 2,
+          bool F8 = false>
 hipError_t launch_pipe(const void* e, int64_t M, int N, int K, const void* W,
                        const EpiArgs& ep, hipStream_t s, int splits = 1) {
-  static_assert(PipeCfg<BM, BN, BK, S>::kLdsBytes * MINB <= 160 * 1024, "LDS per CU");
+  static_assert(PipeCfg<BM, BN, BK * (F8 ? 1 : 2), S>::kLdsBytes * MINB <= 160 * 1024,
+                "LDS per CU");
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, BK, S, EPI, MINB, WGM, WGN>),
+  hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, S, EPI, MINB, WGM, WGN, F8>),
                      dim3((unsigned)blocks, (unsigned)splits), dim3(64 * WGM * WGN), 0, s,
-                     static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), M, N, K,
+                     static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), M, N, K,
                      ep);
   return hipGetLastError();
 }
@@ -808,6 +849,28 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
   return hipGetLastError();
 }
 
+// Scalar gate on FP8 operands: e8 [N][E] = E4M3(e 2^se), W8 [d][E] =
+// E4M3(W 2^sw); E a multiple of 128 (checked by the caller).
+hipError_t launch_project_scalar_fp8(const void* e8, int64_t N, int64_t E, const void* W8,
+                                     int64_t d, float g, const void* resid, void* out,
+                                     int se, int sw, hipStream_t s) {
+  EpiArgs ep{};
+  ep.g = g;
+  ep.resid = static_cast<const uint16_t*>(resid);
+  ep.out = static_cast<uint16_t*>(out);
+  ep.f8_sa = 127 - sw;
+  ep.f8_sb = 127 - se;
+  auto cost = [&](int64_t bn) {
+    const int64_t blocks = ((N + 255) / 256) * ((d + bn - 1) / bn);
+    return ((blocks + 255) / 256) * bn;
+  };
+  if (cost(192) < cost(256))
+    return launch_pipe<256, 192, kPipeBK8, kPipeStages, 1, EPI_SCALAR, 4, 2, true>(
+        e8, N, (int)d, (int)E, W8, ep, s);
+  return launch_pipe<256, 256, kPipeBK8, kPipeStages, 1, EPI_SCALAR, 2, 4, true>(
+      e8, N, (int)d, (int)E, W8, ep, s);
+}
+
 // out[s][M][N] (fp32, row stride ldo) = g * A[M][s Kc .. (s+1) Kc) . B[N][same]^T
 // for s < splits: bf16 operands with row strides lda / ldb; Kc a multiple of
 // 64 (checked by the caller).
@@ -823,11 +886,13 @@ hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64
   return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_F32, 2, 4>(A, M, N, Kc, B, ep, s, splits);
 }
 
-// Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller).
+// Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller; E %
+// 128 == 0 for FP8 operands, f8 = 1 with scales se, sw).
 hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
                                int64_t d, int64_t Mbr, const void* h,
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
-                               float* part_v, float* part_k, hipStream_t s) {
+                               float* part_v, float* part_k, int f8, int se, int sw,
+                               hipStream_t s) {
   EpiArgs ep{};
   ep.d = (int)d;
   ep.n_cb = (int)(d / kColBlock);
@@ -837,6 +902,12 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
+  if (f8) {
+    ep.f8_sa = 127 - sw;
+    ep.f8_sb = 127 - se;
+    return launch_pipe<256, 256, kPipeBK8, kPipeStages, 1, EPI_ENGRAM, 2, 4, true>(
+        e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
+  }
   return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM, 2, 4>(e, N, (int)((1 + Mbr) * d),
                                                                    (int)E, W, ep, s);
 }

@@ -101,6 +101,89 @@ __device__ __forceinline__ void store_chunk(const Raw& x, uint32_t sbits,
   }
 }
 
+// The same chunk written as E4M3(e 2^s) bytes (qs = 2^s): the e value is
+// the one the bf16 / fp32 path stores (sign applied; NF4 rounded to bf16
+// first), scaled exactly and converted by f32_to_e4m3. epc bytes out.
+template <int DT>
+__device__ __forceinline__ void store_chunk_fp8(const Raw& x, uint32_t sbits,
+                                                uint8_t* __restrict__ dst, const float* cb,
+                                                float qs) {
+  if constexpr (DT == PG_F32) {
+    const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
+    uint32_t o = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      o |= f32_to_e4m3(__uint_as_float(w[h] ^ (((sbits >> h) & 1u) << 31)) * qs) << (8 * h);
+    *reinterpret_cast<uint32_t*>(dst) = o;
+  } else if constexpr (DT == PG_BF16) {
+    const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const uint32_t b = (h & 1) ? (w[h >> 1] >> 16) : (w[h >> 1] & 0xFFFFu);
+      const float v = __uint_as_float((b ^ (((sbits >> h) & 1u) << 15)) << 16);
+      o[h >> 2] |= f32_to_e4m3(v * qs) << (8 * (h & 3));
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+  } else {
+    const uint32_t wds[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = 0u;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const uint32_t byte = (wds[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+      const uint32_t blo = f32_to_bf16(__fmul_rn(cb[byte & 15u], x.scale)) ^
+                           (((sbits >> (2 * b)) & 1u) << 15);
+      const uint32_t bhi = f32_to_bf16(__fmul_rn(cb[byte >> 4], x.scale)) ^
+                           (((sbits >> (2 * b + 1)) & 1u) << 15);
+      const uint32_t lo8 = f32_to_e4m3(__uint_as_float(blo << 16) * qs);
+      const uint32_t hi8 = f32_to_e4m3(__uint_as_float(bhi << 16) * qs);
+      o[b >> 1] |= (lo8 | (hi8 << 8)) << (16 * (b & 1));
+    }
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// dst[i] = E4M3(src[i] qs) for bf16 or fp32 src; a thread converts 8
+// consecutive elements (16 or 32 input bytes, 8 output bytes).
+__global__ __launch_bounds__(kThreads) void quantize_fp8_kernel(const void* __restrict__ src,
+                                                                int dt, int64_t n, float qs,
+                                                                uint8_t* __restrict__ dst) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; i < n; i += stride) {
+    float v[8];
+    const int cnt = n - i < 8 ? (int)(n - i) : 8;
+    if (cnt == 8) {
+      if (dt == PG_BF16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          v[h] = __uint_as_float(((h & 1) ? (ww[h >> 1] >> 16) : (ww[h >> 1] & 0xFFFFu)) << 16);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+      uint32_t o[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) o[h >> 2] |= f32_to_e4m3(v[h] * qs) << (8 * (h & 3));
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(o[0], o[1]);
+    } else {
+      for (int h = 0; h < cnt; ++h) {
+        const float x = dt == PG_BF16
+                            ? bf16_to_f32(static_cast<const uint16_t*>(src)[i + h])
+                            : static_cast<const float*>(src)[i + h];
+        dst[i + h] = (uint8_t)f32_to_e4m3(x * qs);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void index_kernel(
     DevLayout L, const int32_t* __restrict__ tokens, int64_t B, int64_t T,
     const int32_t* __restrict__ cmap, int64_t V, int32_t* __restrict__ canon_out,
@@ -188,12 +271,13 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   }
 }
 
-template <int DT>
+// F8: e leaves as E4M3(e qs) bytes.
+template <int DT, bool F8>
 __global__ __launch_bounds__(kThreads) void index_gather_kernel(
     DevLayout L, int TB, int C, const int32_t* __restrict__ tokens, int64_t B, int64_t T,
     const int32_t* __restrict__ cmap, int64_t V, const uint8_t* __restrict__ table,
     const __half* __restrict__ scales, uint8_t* __restrict__ e_out,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, float qs) {
   __shared__ uint64_t rc[kMaxRoles * kRoleStride];
   __shared__ int64_t rowsL[kThreads];
   __shared__ uint64_t signsL[kThreads * kMaxSignWords];
@@ -248,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void index_gather_kernel(
     }
   }
   __syncthreads();
-  constexpr int OB = Chunk<DT>::out_bytes;
+  constexpr int OB = F8 ? Chunk<DT>::epc : Chunk<DT>::out_bytes;
   const int row_bytes = C * 16;
   const int64_t ntok = (N - tok0) < TB ? (N - tok0) : TB;
   const int tasks = (int)ntok * OK * C;
@@ -270,7 +354,10 @@ __global__ __launch_bounds__(kThreads) void index_gather_kernel(
     for (int u = 0; u < kBatch; ++u) {
       if (qq[u] < 0) continue;
       const uint32_t sb = L.use_signs ? chunk_sign_bits<DT>(signsL + qq[u] * L.W, cc[u]) : 0u;
-      store_chunk<DT>(raw[u], sb, eb + ((int64_t)qq[u] * C + cc[u]) * OB, cb);
+      if constexpr (F8)
+        store_chunk_fp8<DT>(raw[u], sb, eb + ((int64_t)qq[u] * C + cc[u]) * OB, cb, qs);
+      else
+        store_chunk<DT>(raw[u], sb, eb + ((int64_t)qq[u] * C + cc[u]) * OB, cb);
     }
   }
 }
@@ -323,7 +410,7 @@ hipError_t launch_gather(const DevLayout& L, int32_t dt, const void* table,
 hipError_t launch_index_gather(const DevLayout& L, int32_t dt, const void* table,
                                const void* scales, const int32_t* tokens, int64_t B,
                                int64_t T, const int32_t* cmap, int64_t V, void* e_out,
-                               int32_t* status, hipStream_t s) {
+                               int32_t* status, int e_fp8, int e_scale_exp, hipStream_t s) {
   const int C = chunks_per_row(dt, L.r);
   const int OK = L.O * L.K;
   const int TB = kThreads / OK;  // tokens per block (O*K <= 64 is validated)
@@ -332,15 +419,30 @@ hipError_t launch_index_gather(const DevLayout& L, int32_t dt, const void* table
   const auto* tb = static_cast<const uint8_t*>(table);
   const auto* sc = static_cast<const __half*>(scales);
   auto* eo = static_cast<uint8_t*>(e_out);
-  if (dt == PG_F32)
-    hipLaunchKernelGGL(index_gather_kernel<PG_F32>, dim3((unsigned)blocks), dim3(kThreads),
-                       0, s, L, TB, C, tokens, B, T, cmap, V, tb, sc, eo, status);
-  else if (dt == PG_BF16)
-    hipLaunchKernelGGL(index_gather_kernel<PG_BF16>, dim3((unsigned)blocks), dim3(kThreads),
-                       0, s, L, TB, C, tokens, B, T, cmap, V, tb, sc, eo, status);
-  else
-    hipLaunchKernelGGL(index_gather_kernel<PG_NF4>, dim3((unsigned)blocks), dim3(kThreads),
-                       0, s, L, TB, C, tokens, B, T, cmap, V, tb, sc, eo, status);
+  const float qs = ldexpf(1.0f, e_scale_exp);
+#define PG_IG(DT, F8)                                                                     \
+  hipLaunchKernelGGL((index_gather_kernel<DT, F8>), dim3((unsigned)blocks), dim3(kThreads), \
+                     0, s, L, TB, C, tokens, B, T, cmap, V, tb, sc, eo, status, qs)
+  if (e_fp8) {
+    if (dt == PG_F32) PG_IG(PG_F32, true);
+    else if (dt == PG_BF16) PG_IG(PG_BF16, true);
+    else PG_IG(PG_NF4, true);
+  } else {
+    if (dt == PG_F32) PG_IG(PG_F32, false);
+    else if (dt == PG_BF16) PG_IG(PG_BF16, false);
+    else PG_IG(PG_NF4, false);
+  }
+#undef PG_IG
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, int scale_exp,
+                               uint8_t* dst, hipStream_t s) {
+  int64_t blocks = (n + kThreads * 8 - 1) / (kThreads * 8);
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, src,
+                     (int)src_dtype, n, ldexpf(1.0f, scale_exp), dst);
   return hipGetLastError();
 }
 

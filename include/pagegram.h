@@ -244,6 +244,65 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
                       void* workspace, int64_t workspace_bytes,
                       int32_t* dev_status, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 operands (Engram notes §3.4: the value and key projections run as one
+ * dense FP8 GEMM). Format: OCP E4M3 (sign, 4-bit exponent of bias 7, 3-bit
+ * mantissa, no infinities, 0x7F / 0xFF NaN, largest finite 448). A tensor
+ * is stored as q = E4M3(v * 2^s) with one power-of-two scale exponent s per
+ * tensor chosen by the caller (|s| <= 64): rounded to nearest, ties to the
+ * even mantissa; magnitudes at or above 448 saturate to 448; NaN stays NaN;
+ * the sign of zero is kept. The projection multiplies the dequantised
+ * operands q 2^-s on the matrix cores with fp32 accumulation; residual and
+ * output stay bf16.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * pg_quantize_fp8 -- dst[i] = E4M3(src[i] * 2^scale_exp), i < n (W, say).
+ *   src  [n] device, PG_BF16 or PG_F32 (src_dtype), 16-byte aligned
+ *   dst  [n] device bytes, 16-byte aligned
+ */
+PG_API int pg_quantize_fp8(const void* src, int32_t src_dtype, int64_t n,
+                           int32_t scale_exp, uint8_t* dst, hipStream_t stream);
+
+/*
+ * pg_index_gather_fp8 -- pg_index_gather writing e as E4M3 bytes:
+ * e_out[t][j] = E4M3(e[t][j] * 2^e_scale_exp), where e is the value
+ * pg_index_gather stores (bf16 for bf16 and NF4 tables -- NF4 rounded to
+ * bf16 first -- fp32 for an fp32 table). e_out [B*T][e_dim] device bytes,
+ * 16-byte aligned.
+ */
+PG_API int pg_index_gather_fp8(const pg_layout* layout, const pg_table* table,
+                               const int32_t* tokens, int64_t B, int64_t T,
+                               const int32_t* canon_map, int64_t V,
+                               int32_t e_scale_exp, uint8_t* e_out,
+                               int32_t* dev_status, hipStream_t stream);
+
+/*
+ * pg_project_gate_fp8 -- pg_project_gate on E4M3 operands:
+ *   e8  [N][e_dim] = E4M3(e 2^e_scale_exp), W8 [d_out][e_dim] =
+ *   E4M3(W 2^w_scale_exp) (device bytes); resid / out bf16 as in
+ *   pg_project_gate (fuse->dtype must be PG_BF16); e_dim a multiple of 128;
+ *   workspace as for pg_project_gate. PG_EUNSUPPORTED otherwise.
+ */
+PG_API int pg_project_gate_fp8(const pg_fuse* fuse, const uint8_t* e8, int64_t B,
+                               int64_t T, int64_t e_dim, const uint8_t* W8,
+                               int32_t e_scale_exp, int32_t w_scale_exp,
+                               const void* resid, void* out, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pg_forward_fp8 -- pg_index_gather_fp8 followed by pg_project_gate_fp8;
+ * workspace at least pg_workspace_size(layout, fuse, B, T) bytes (256-byte
+ * aligned; e takes one byte per element here).
+ */
+PG_API int pg_forward_fp8(const pg_layout* layout, const pg_table* table,
+                          const pg_fuse* fuse, const int32_t* tokens, int64_t B,
+                          int64_t T, const int32_t* canon_map, int64_t V,
+                          const uint8_t* W8, int32_t e_scale_exp,
+                          int32_t w_scale_exp, const void* resid, void* out,
+                          void* workspace, int64_t workspace_bytes,
+                          int32_t* dev_status, hipStream_t stream);
+
 /* Message for a pg_status value (static storage). */
 PG_API const char* pg_strerror(int status);
 
