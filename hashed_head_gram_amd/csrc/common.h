@@ -146,27 +146,22 @@ __device__ __forceinline__ uint64_t sign_word(const DevLayout& L, const uint64_t
 // ---------------------------------------------------------------------------
 // Float helpers
 
-// fp32 -> OCP E4M3 (sign, 4-bit exponent of bias 7, 3-bit mantissa; no
-// infinities; 0x7F / 0xFF NaN; largest finite 448): round to nearest, ties
-// to the even mantissa, magnitudes >= 448 saturate to 448, NaN stays NaN,
-// the sign of zero is kept. Integer arithmetic on the fp32 bits.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448, infinities
-  if (a < 0x3C800000u) {                             // |x| < 2^-6: subnormal codes
-    // q = |x| 2^9 rounded to nearest even (exact scaling); q = 8 is the
-    // smallest normal, code 0x08
-    const uint32_t q = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | q;
-  }
-  // normal: bits 30..20 hold (exponent << 3 | top 3 mantissa bits); round
-  // to nearest even at bit 20, then rebias the exponent from 127 to 7
-  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-  const uint32_t code = r - (120u << 3);
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
+// Two fp32 values -> OCP E4M3 bytes (a in bits 0-7, b in bits 8-15). E4M3:
+// sign, 4-bit exponent of bias 7, 3-bit mantissa, no infinities, 0x7F / 0xFF
+// NaN, largest finite 448. Rounded to nearest, ties to the even mantissa;
+// magnitudes >= 448 (infinities included) saturate to 448; NaN stays NaN
+// with its sign; the sign of zero is kept. v_cvt_pk_fp8_f32 rounds to
+// nearest even but turns overflow into NaN and NaN into 0xFF, so the values
+// are clamped to +-448 first (v_med3) and NaN codes are set afterwards.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+  const uint32_t na = 0x7Fu | ((__float_as_uint(a) >> 24) & 0x80u);
+  const uint32_t nb = 0x7Fu | ((__float_as_uint(b) >> 24) & 0x80u);
+  r = (a != a) ? ((r & 0xFF00u) | na) : r;
+  r = (b != b) ? ((r & 0x00FFu) | (nb << 8)) : r;
+  return r;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -103,26 +103,28 @@ __device__ __forceinline__ void store_chunk(const Raw& x, uint32_t sbits,
 
 // The same chunk written as E4M3(e 2^s) bytes (qs = 2^s): the e value is
 // the one the bf16 / fp32 path stores (sign applied; NF4 rounded to bf16
-// first), scaled exactly and converted by f32_to_e4m3. epc bytes out.
+// first), scaled exactly and converted by f32x2_to_e4m3. epc bytes out.
 template <int DT>
 __device__ __forceinline__ void store_chunk_fp8(const Raw& x, uint32_t sbits,
                                                 uint8_t* __restrict__ dst, const float* cb,
                                                 float qs) {
   if constexpr (DT == PG_F32) {
     const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
-    uint32_t o = 0;
+    float v[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      o |= f32_to_e4m3(__uint_as_float(w[h] ^ (((sbits >> h) & 1u) << 31)) * qs) << (8 * h);
-    *reinterpret_cast<uint32_t*>(dst) = o;
+    for (int h = 0; h < 4; ++h) v[h] = __uint_as_float(w[h] ^ (((sbits >> h) & 1u) << 31)) * qs;
+    *reinterpret_cast<uint32_t*>(dst) = f32x2_to_e4m3(v[0], v[1]) | (f32x2_to_e4m3(v[2], v[3]) << 16);
   } else if constexpr (DT == PG_BF16) {
     const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
     uint32_t o[2] = {0u, 0u};
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const uint32_t b = (h & 1) ? (w[h >> 1] >> 16) : (w[h >> 1] & 0xFFFFu);
-      const float v = __uint_as_float((b ^ (((sbits >> h) & 1u) << 15)) << 16);
-      o[h >> 2] |= f32_to_e4m3(v * qs) << (8 * (h & 3));
+    for (int q = 0; q < 4; ++q) {
+      // elements 2q (low half) and 2q + 1 (high half) of the chunk
+      const uint32_t sw = w[q] ^ (((sbits >> (2 * q)) & 1u) << 15) ^
+                          (((sbits >> (2 * q + 1)) & 1u) << 31);
+      const float lo = __uint_as_float(sw << 16) * qs;
+      const float hi = __uint_as_float(sw & 0xFFFF0000u) * qs;
+      o[q >> 1] |= f32x2_to_e4m3(lo, hi) << (16 * (q & 1));
     }
     *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
   } else {
@@ -137,9 +139,8 @@ __device__ __forceinline__ void store_chunk_fp8(const Raw& x, uint32_t sbits,
                            (((sbits >> (2 * b)) & 1u) << 15);
       const uint32_t bhi = f32_to_bf16(__fmul_rn(cb[byte >> 4], x.scale)) ^
                            (((sbits >> (2 * b + 1)) & 1u) << 15);
-      const uint32_t lo8 = f32_to_e4m3(__uint_as_float(blo << 16) * qs);
-      const uint32_t hi8 = f32_to_e4m3(__uint_as_float(bhi << 16) * qs);
-      o[b >> 1] |= (lo8 | (hi8 << 8)) << (16 * (b & 1));
+      o[b >> 1] |= f32x2_to_e4m3(__uint_as_float(blo << 16) * qs,
+                                 __uint_as_float(bhi << 16) * qs) << (16 * (b & 1));
     }
     uint4* d4 = reinterpret_cast<uint4*>(dst);
     d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -171,14 +172,15 @@ __global__ __launch_bounds__(kThreads) void quantize_fp8_kernel(const void* __re
       }
       uint32_t o[2] = {0u, 0u};
 #pragma unroll
-      for (int h = 0; h < 8; ++h) o[h >> 2] |= f32_to_e4m3(v[h] * qs) << (8 * (h & 3));
+      for (int h = 0; h < 8; h += 2)
+        o[h >> 2] |= f32x2_to_e4m3(v[h] * qs, v[h + 1] * qs) << (8 * (h & 3));
       *reinterpret_cast<uint2*>(dst + i) = make_uint2(o[0], o[1]);
     } else {
       for (int h = 0; h < cnt; ++h) {
         const float x = dt == PG_BF16
                             ? bf16_to_f32(static_cast<const uint16_t*>(src)[i + h])
                             : static_cast<const float*>(src)[i + h];
-        dst[i + h] = (uint8_t)f32_to_e4m3(x * qs);
+        dst[i + h] = (uint8_t)(f32x2_to_e4m3(x * qs, 0.0f) & 0xFFu);
       }
     }
   }
