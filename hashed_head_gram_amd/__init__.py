@@ -57,6 +57,10 @@ _SIGS = {
                                _vp, _i64, _vp]),
     "pg_forward": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                           _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pg_stage_geometry": (_i32, [_P(PgLayout), _i32, _i64, _P(_i64), _P(_i64), _P(_i64)]),
+    "pg_stage_rows": (_i32, [_P(PgLayout), _P(PgTable), _vp, _i64, _P(PgTable), _vp, _vp, _vp,
+                             _vp, _i64, _vp]),
+    "pg_gather_staged": (_i32, [_P(PgLayout), _P(PgTable), _vp, _vp, _i64, _i32, _vp, _vp]),
     "pg_quantize_fp8": (_i32, [_vp, _i32, _i64, _i32, _vp, _vp]),
     "pg_index_gather_fp8": (_i32, [_P(PgLayout), _P(PgTable), _vp, _i64, _i64, _vp,
                                    _i64, _i32, _vp, _vp, _vp]),
@@ -230,6 +234,34 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# Staging from a host-resident table
+
+
+def pg_stage_geometry(layout, table_dtype, n_tok):
+    """(rows per unit, most units per step, workspace bytes)."""
+    u, m, w = _i64(), _i64(), _i64()
+    _check("pg_stage_geometry", lib().pg_stage_geometry(
+        ctypes.byref(layout), table_dtype, int(n_tok), ctypes.byref(u), ctypes.byref(m),
+        ctypes.byref(w)))
+    return u.value, m.value, w.value
+
+
+def pg_stage_rows(layout, src, rows, cache, cache_rows, n_units, workspace, unit_first=None,
+                  stream=None):
+    """rows int64 [N, O, K] (device); src / cache pg_table structures."""
+    _check("pg_stage_rows", lib().pg_stage_rows(
+        ctypes.byref(layout), ctypes.byref(src), _ptr(rows), rows.shape[0], ctypes.byref(cache),
+        _ptr(cache_rows), _ptr(n_units), _ptr(unit_first), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pg_gather_staged(layout, cache, cache_rows, signs, e_dtype, e_out, stream=None):
+    _check("pg_gather_staged", lib().pg_gather_staged(
+        ctypes.byref(layout), ctypes.byref(cache), _ptr(cache_rows), _ptr(signs),
+        cache_rows.shape[0], e_dtype, _ptr(e_out), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

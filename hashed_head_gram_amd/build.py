@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagegram.so")
-SOURCES = ["api.hip", "index.hip", "gemm.hip", "engram.hip", "backward.hip", "pagesim.cpp"]
+SOURCES = ["api.hip", "index.hip", "gemm.hip", "engram.hip", "backward.hip", "stage.hip",
+           "pagesim.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -325,6 +325,103 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
 }
 
 // ---------------------------------------------------------------------------
+// Staging from a host-resident table
+
+namespace {
+
+// Rows per staging unit: a PageGram page, or the Engram-style tables'
+// 4 KiB run (row bytes: fp32 4r, bf16 2r, NF4 r/2 codes + 2 scale bytes).
+int64_t stage_unit_rows(const DevLayout& L, int32_t dt) {
+  if (L.kind == PG_PAGEGRAM) return (int64_t)L.K * (int64_t)L.S;
+  const int64_t rb = dt == PG_F32 ? 4 * L.r : dt == PG_BF16 ? 2 * L.r : L.r / 2 + 2;
+  const int64_t u = 4096 / rb;
+  return u < 1 ? 1 : u;
+}
+
+int64_t data_row_bytes(const DevLayout& L, int32_t dt) {
+  return dt == PG_F32 ? 4 * L.r : dt == PG_BF16 ? 2 * L.r : L.r / 2;
+}
+
+// Table fields of a cache (any row count) for the layout.
+int check_cache(const DevLayout& L, const pg_table* t, int32_t dt) {
+  if (!t || !t->data || !aligned(t->data, 16) || t->dtype != dt || t->n_rows < 1)
+    return PG_EINVAL;
+  if (dt == PG_NF4 && (!t->scales || !aligned(t->scales, 2))) return PG_EINVAL;
+  return PG_OK;
+}
+
+}  // namespace
+
+PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64_t n_tok,
+                             int64_t* unit_rows, int64_t* max_units, int64_t* workspace_bytes) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  if (table_dtype != PG_F32 && table_dtype != PG_BF16 && table_dtype != PG_NF4) return PG_EINVAL;
+  if (n_tok < 0) return PG_EINVAL;
+  if (n_tok > kMaxTokens) return PG_ERANGE;
+  const int64_t U = stage_unit_rows(L, table_dtype);
+  if (U > INT_MAX) return PG_EUNSUPPORTED;
+  const pg::StagePlan p = pg::stage_plan(L, (int)U, n_tok);
+  if (p.H > ((int64_t)1 << 31)) return PG_ERANGE;
+  if (unit_rows) *unit_rows = U;
+  if (max_units) *max_units = p.max_units;
+  if (workspace_bytes) *workspace_bytes = p.bytes;
+  return PG_OK;
+}
+
+PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, const int64_t* rows,
+                         int64_t n_tok, const pg_table* cache, int64_t* cache_rows,
+                         int64_t* n_units, int64_t* unit_first, void* workspace,
+                         int64_t workspace_bytes, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, src);
+  if (st != PG_OK) return st;
+  st = check_cache(L, cache, src->dtype);
+  if (st != PG_OK) return st;
+  int64_t U = 0, max_units = 0, ws_bytes = 0;
+  st = pg_stage_geometry(layout, src->dtype, n_tok, &U, &max_units, &ws_bytes);
+  if (st != PG_OK) return st;
+  if (!n_units) return PG_EINVAL;
+  if (n_tok == 0) return hip_status(pg::launch_set_i64(n_units, 0, stream));
+  if (!rows || !cache_rows) return PG_EINVAL;
+  if (cache->n_rows < max_units * U) return PG_EINVAL;
+  if (!workspace || workspace_bytes < ws_bytes || !aligned(workspace, 256)) return PG_EINVAL;
+  const pg::StagePlan p = pg::stage_plan(L, (int)U, n_tok);
+  return hip_status(pg::launch_stage(L, p, (int)data_row_bytes(L, src->dtype), src->data,
+                                     src->scales, rows, const_cast<void*>(cache->data),
+                                     const_cast<void*>(cache->scales), cache_rows, n_units,
+                                     unit_first, workspace, stream));
+}
+
+PG_API int pg_gather_staged(const pg_layout* layout, const pg_table* cache,
+                            const int64_t* cache_rows, const uint64_t* signs, int64_t n_tok,
+                            int32_t e_dtype, void* e_out, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  if (!cache) return PG_EINVAL;
+  st = check_cache(L, cache, cache->dtype);
+  if (st != PG_OK) return st;
+  // the table's per-dtype row constraints, checked on a view with the
+  // layout's row count
+  pg_table view = *cache;
+  view.n_rows = L.n_rows;
+  st = check_table(L, &view);
+  if (st != PG_OK) return st;
+  if (e_dtype != table_e_dtype(cache->dtype)) return PG_EUNSUPPORTED;
+  if (n_tok < 0) return PG_EINVAL;
+  if (n_tok == 0) return PG_OK;
+  if (!cache_rows || !signs || !e_out || !aligned(e_out, 16)) return PG_EINVAL;
+  DevLayout LC = L;
+  LC.n_rows = cache->n_rows;             // gather rows are clamped into the cache
+  return hip_status(pg::launch_gather(LC, cache->dtype, cache->data, cache->scales, cache_rows,
+                                      signs, n_tok, e_out, stream));
+}
+
+// ---------------------------------------------------------------------------
 // FP8 (E4M3) operands
 
 PG_API int pg_quantize_fp8(const void* src, int32_t src_dtype, int64_t n, int32_t scale_exp,

@@ -237,6 +237,21 @@ hipError_t launch_rms_step(const int64_t* urows, const float* ugrad, const int64
 hipError_t launch_rms_flush(int64_t R, int r, float* table, float* vhat, int64_t* last,
                             int64_t step, float lr, float beta2, float wd, hipStream_t s);
 
+// Staging of table units into an HBM cache (stage.hip): workspace geometry
+// for n_tok tokens with units of U rows, then the launcher. rb: bytes of a
+// row in the data array (NF4: the r/2 code bytes; scales are separate).
+struct StagePlan {
+  int U;
+  int64_t n_look, max_units, H, nb;
+  int64_t off_keys, off_ranks, off_bcount, off_ufirst, off_ucount;
+  int64_t bytes;
+};
+StagePlan stage_plan(const DevLayout& L, int U, int64_t n_tok);
+hipError_t launch_stage(const DevLayout& L, const StagePlan& p, int rb, const void* src,
+                        const void* src_scales, const int64_t* rows, void* dst,
+                        void* dst_scales, int64_t* cache_rows, int64_t* n_units,
+                        int64_t* ufirst_out, void* workspace, hipStream_t s);
+
 // Engram fusion (bf16 or, with f8, E4M3 operands of scales se, sw): workspace
 // layout described in engram_workspace_bytes.
 int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M);

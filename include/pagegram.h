@@ -245,6 +245,57 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
                       int32_t* dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Staging from a host-resident table (PageGram tech report §3.3, Engram
+ * notes §3.5: addresses depend only on token IDs and are known before the
+ * layer runs, so the touched parts of a table kept in host memory can be
+ * fetched ahead). The unit of transfer is a PageGram page (K*S rows, shared
+ * by the K heads of a token-order) or, for the Engram-style tables, a run of
+ * floor(4096 / row_bytes) rows of one per-head table starting at that
+ * table's first row (row_bytes: fp32 4r, bf16 2r, NF4 r/2 + 2).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * pg_stage_geometry -- rows per unit U, the most units a step of n_tok tokens
+ * can touch (n_tok * orders for PageGram, n_tok * orders * K otherwise), and
+ * the device workspace bytes of pg_stage_rows. Outputs are host pointers,
+ * each nullable.
+ */
+PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64_t n_tok,
+                             int64_t* unit_rows, int64_t* max_units,
+                             int64_t* workspace_bytes);
+
+/*
+ * pg_stage_rows -- copy every unit that rows touch, once, from src into a
+ * device cache, and rewrite the rows for it.
+ *   src         the whole table (pg_table as above); data (and NF4 scales)
+ *               must be readable by the device: device memory, or pinned
+ *               host memory allocated with hipHostMalloc
+ *   rows        [n_tok][orders][K] int64 device (pg_index's rows_out)
+ *   cache       device table of src's dtype with n_rows >= max_units * U;
+ *               unit s of the step occupies rows [s U, s U + its rows)
+ *   cache_rows  [n_tok][orders][K] int64 device: the row of each lookup in
+ *               the cache (cache row cache_rows[q] holds table row rows[q])
+ *   n_units     int64 device: the number of units staged
+ *   unit_first  int64 device [max_units], nullable: first table row of the
+ *               unit in each slot (slots follow a deterministic order)
+ *   workspace   pg_stage_geometry bytes of device memory, 256-byte aligned
+ * Rows outside [0, R) are clamped into the table.
+ */
+PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, const int64_t* rows,
+                         int64_t n_tok, const pg_table* cache, int64_t* cache_rows,
+                         int64_t* n_units, int64_t* unit_first, void* workspace,
+                         int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pg_gather_staged -- pg_gather from a cache filled by pg_stage_rows: e from
+ * (cache, cache_rows, signs) equals pg_gather's e from (table, rows, signs)
+ * bit for bit. cache->n_rows is the cache's own row count.
+ */
+PG_API int pg_gather_staged(const pg_layout* layout, const pg_table* cache,
+                            const int64_t* cache_rows, const uint64_t* signs, int64_t n_tok,
+                            int32_t e_dtype, void* e_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * FP8 operands (Engram notes §3.4: the value and key projections run as one
  * dense FP8 GEMM). Format: OCP E4M3 (sign, 4-bit exponent of bias 7, 3-bit
  * mantissa, no infinities, 0x7F / 0xFF NaN, largest finite 448). A tensor
