@@ -63,6 +63,12 @@ def parse():
                    help="flash page-cache figures (reads/token under an LRU RAM cache) "
                         "of the 20B NF4 table in the PageGram S=4, S=15 and Engram-style "
                         "layouts, from pg_index rows of the token pool")
+    p.add_argument("--host-table", action="store_true",
+                   help="table in pinned host memory: pg_index, pg_stage_rows (touched units "
+                        "to an HBM cache), pg_gather_staged, pg_project_gate per step, "
+                        "sequential and with the next step's staging on a second stream")
+    p.add_argument("--stage-unit", choices=["page", "row"], default="page",
+                   help="--host-table unit of transfer: pages / 4 KiB runs, or single rows")
     p.add_argument("--fp8", action="store_true",
                    help="E4M3 projection operands (pg_forward_fp8); a separate line")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -374,6 +380,174 @@ def cpu_baseline(wl, n_tok):
                       f"{blas} BLAS threads"}
 
 
+def host_table_bench(args):
+    """Scalar-gate step with the table in pinned host memory: staged bytes
+    per token and tokens/s, sequential and pipelined (the next step's index
+    + staging on a second stream under this step's gather + projection,
+    double-buffered caches)."""
+    import numpy as np
+    import torch
+
+    import hashed_head_gram_amd as pg
+    import synth
+    from synth import configs, device as sdev
+
+    dev = torch.device("cuda:0")
+    wl = configs.workload(args.workload)
+    if wl["gate"] != "scalar" or wl["act_dtype"] != "bf16":
+        sys.exit("--host-table: scalar-gate bf16 workloads")
+    lay_d = wl["layout"]
+    layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
+                            pages=lay_d["pages"], head_rows=lay_d["head_rows"],
+                            hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
+                            n_min=lay_d["n_min"], n_max=lay_d["n_max"],
+                            pad_id=wl["canon_vocab"])
+    R = pg.pg_layout_rows(layout)
+    r, K = lay_d["r"], lay_d["K"]
+    O = lay_d["n_max"] - lay_d["n_min"] + 1
+    B, T = wl["B"], wl["T"]
+    N, E, d = B * T, O * K * r, wl["d"]
+    nf4 = wl["table_dtype"] == "nf4"
+    dt = pg.PG_NF4 if nf4 else pg.PG_BF16
+    # table filled on the device, then kept only in pinned host memory
+    if nf4:
+        dc = torch.empty(R, r // 2, dtype=torch.uint8, device=dev)
+        dsc = torch.empty(R, dtype=torch.float16, device=dev)
+        sdev.fill_nf4_table(dc, dsc, wl["table_seed"])
+        hc = torch.empty(R, r // 2, dtype=torch.uint8, pin_memory=True)
+        hsc = torch.empty(R, dtype=torch.float16, pin_memory=True)
+        hc.copy_(dc)
+        hsc.copy_(dsc)
+        del dc, dsc
+        src = pg.make_table(dt, hc, R, scales=hsc)
+        row_b = r // 2 + 2
+    else:
+        dtab = torch.empty(R, r, dtype=torch.bfloat16, device=dev)
+        sdev.fill_normal(dtab, wl["table_seed"], configs.STREAM_TABLE, wl["table_sigma"])
+        htab = torch.empty(R, r, dtype=torch.bfloat16, pin_memory=True)
+        htab.copy_(dtab)
+        del dtab
+        src = pg.make_table(dt, htab, R)
+        row_b = 2 * r
+    torch.cuda.empty_cache()
+    cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
+    pool = [torch.from_numpy(synth.tokens(wl, batch=j)).to(dev) for j in range(POOL)]
+    W = torch.empty(d, E, dtype=torch.bfloat16, device=dev)
+    sdev.fill_normal(W, wl["data_seed"], configs.STREAM_W, wl["w_sigma"])
+    x = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+    sdev.fill_normal(x, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
+    fuse = pg.make_fuse(pg.PG_GATE_SCALAR, pg.PG_BF16, d, g=wl["g"])
+    uk = pg.PG_STAGE_ROW if args.stage_unit == "row" else pg.PG_STAGE_PAGE
+    U, max_units, wsb = pg.pg_stage_geometry(layout, dt, N, unit_kind=uk)
+
+    def buffers():
+        b = dict(rows=torch.empty(N, O, K, dtype=torch.int64, device=dev),
+                 signs=torch.empty(N, O, K, (r + 63) // 64, dtype=torch.int64, device=dev),
+                 crows=torch.empty(N, O, K, dtype=torch.int64, device=dev),
+                 nu=torch.zeros(1, dtype=torch.int64, device=dev),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev),
+                 e=torch.empty(N, E, dtype=torch.bfloat16, device=dev),
+                 out=torch.empty(N, d, dtype=torch.bfloat16, device=dev))
+        if nf4:
+            b["cd"] = torch.empty(max_units * U, r // 2, dtype=torch.uint8, device=dev)
+            b["cs"] = torch.empty(max_units * U, dtype=torch.float16, device=dev)
+            b["cache"] = pg.make_table(dt, b["cd"], max_units * U, scales=b["cs"])
+        else:
+            b["cd"] = torch.empty(max_units * U, r, dtype=torch.bfloat16, device=dev)
+            b["cache"] = pg.make_table(dt, b["cd"], max_units * U)
+        return b
+    bufs = [buffers(), buffers()]
+
+    def stage(j, b, stream=None):
+        pg.pg_index(layout, pool[j % POOL], cmap, b["rows"], b["signs"], stream=stream)
+        pg.pg_stage_rows(layout, src, b["rows"], b["cache"], b["crows"], b["nu"], b["ws"],
+                         unit_kind=uk, stream=stream)
+
+    def compute(b, stream=None):
+        pg.pg_gather_staged(layout, b["cache"], b["crows"], b["signs"], pg.PG_BF16, b["e"],
+                            stream=stream)
+        pg.pg_project_gate(fuse, b["e"], B, T, W, x, b["out"], stream=stream)
+
+    # the staged path reproduces the HBM path's e (checked once)
+    stage(0, bufs[0])
+    compute(bufs[0])
+    torch.cuda.synchronize()
+    units = []
+    for j in range(POOL):
+        stage(j, bufs[1])
+        torch.cuda.synchronize()
+        units.append(int(bufs[1]["nu"].item()))
+    unit_b = U * row_b
+    staged_per_tok = float(np.mean(units)) * unit_b / N
+
+    def timed(fn, n):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for j in range(n):
+            fn(j)
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n
+
+    for j in range(args.warmup):
+        stage(j, bufs[0])
+        compute(bufs[0])
+    seq_ms = timed(lambda j: (stage(j, bufs[0]), compute(bufs[0])), args.steps)
+    stage_ms = timed(lambda j: stage(j, bufs[0]), args.steps)
+    comp_ms = timed(lambda j: compute(bufs[0]), args.steps)
+
+    s_st, s_cp = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = [torch.cuda.Event(), torch.cuda.Event()]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def pipelined(n):
+        cur = torch.cuda.current_stream()
+        s_st.wait_stream(cur)
+        s_cp.wait_stream(cur)
+        with torch.cuda.stream(s_st):
+            stage(0, bufs[0], stream=s_st.cuda_stream)
+            ready[0].record(s_st)
+        for j in range(n):
+            b = j % 2
+            if j + 1 < n:
+                with torch.cuda.stream(s_st):
+                    if j >= 1:
+                        s_st.wait_event(done[(j + 1) % 2])
+                    stage(j + 1, bufs[(j + 1) % 2], stream=s_st.cuda_stream)
+                    ready[(j + 1) % 2].record(s_st)
+            with torch.cuda.stream(s_cp):
+                s_cp.wait_event(ready[b])
+                compute(bufs[b], stream=s_cp.cuda_stream)
+                done[b].record(s_cp)
+        cur.wait_stream(s_cp)
+        cur.wait_stream(s_st)
+
+    pipelined(max(args.warmup, 2))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pipelined(args.steps)
+    torch.cuda.synchronize()
+    pipe_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    return {
+        "metric": "M tokens/s with the table in pinned host memory (touched units staged "
+                  "to HBM each step)",
+        "value": N / (pipe_ms / 1e3) / 1e6, "unit": "Mtok/s", "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": pipe_ms,
+        "dtype": "bf16", "data": "synthetic (seeded Zipf token pool, counter-generated table)",
+        "config": {"workload": wl["name"], "tokens": N, "layout": lay_d["kind"],
+                   "table_dtype": wl["table_dtype"], "table_bytes": R * row_b,
+                   "stage_unit": args.stage_unit, "unit_rows": U, "unit_bytes": unit_b},
+        "staged_units_per_step": float(np.mean(units)),
+        "staged_bytes_per_token": staged_per_tok,
+        "sequential_ms_per_step": seq_ms,
+        "index_plus_stage_ms": stage_ms,
+        "gather_plus_project_ms": comp_ms,
+        "host_link_GBps": float(np.mean(units)) * unit_b / (stage_ms / 1e3) / 1e9,
+        "sequential_Mtok_s": N / (seq_ms / 1e3) / 1e6,
+    }
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -381,6 +555,9 @@ def main():
         return
     if args.backward:
         print(json.dumps(backward_bench(args)), flush=True)
+        return
+    if args.host_table:
+        print(json.dumps(host_table_bench(args)), flush=True)
         return
     if args.page_cache:
         line = {"metric": "flash reads per token under an LRU RAM page cache (4 KiB blocks)",

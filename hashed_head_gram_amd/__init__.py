@@ -16,6 +16,7 @@ PG_OK, PG_EINVAL, PG_EUNSUPPORTED, PG_EHIP, PG_ERANGE = 0, -1, -2, -3, -4
 PG_PAGEGRAM, PG_ENGRAM = 0, 1
 PG_F32, PG_BF16, PG_NF4 = 0, 1, 2
 PG_GATE_SCALAR, PG_GATE_ENGRAM = 0, 1
+PG_STAGE_PAGE, PG_STAGE_ROW = 0, 1
 PG_MAX_ORDERS, PG_MAX_HEADS = 4, 16
 
 _i32, _i64, _u64, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -57,9 +58,10 @@ _SIGS = {
                                _vp, _i64, _vp]),
     "pg_forward": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                           _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
-    "pg_stage_geometry": (_i32, [_P(PgLayout), _i32, _i64, _P(_i64), _P(_i64), _P(_i64)]),
-    "pg_stage_rows": (_i32, [_P(PgLayout), _P(PgTable), _vp, _i64, _P(PgTable), _vp, _vp, _vp,
-                             _vp, _i64, _vp]),
+    "pg_stage_geometry": (_i32, [_P(PgLayout), _i32, _i32, _i64, _P(_i64), _P(_i64),
+                                 _P(_i64)]),
+    "pg_stage_rows": (_i32, [_P(PgLayout), _P(PgTable), _i32, _vp, _i64, _P(PgTable), _vp, _vp,
+                             _vp, _vp, _i64, _vp]),
     "pg_gather_staged": (_i32, [_P(PgLayout), _P(PgTable), _vp, _vp, _i64, _i32, _vp, _vp]),
     "pg_quantize_fp8": (_i32, [_vp, _i32, _i64, _i32, _vp, _vp]),
     "pg_index_gather_fp8": (_i32, [_P(PgLayout), _P(PgTable), _vp, _i64, _i64, _vp,
@@ -240,20 +242,22 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
 # Staging from a host-resident table
 
 
-def pg_stage_geometry(layout, table_dtype, n_tok):
-    """(rows per unit, most units per step, workspace bytes)."""
+def pg_stage_geometry(layout, table_dtype, n_tok, unit_kind=0):
+    """(rows per unit, most units per step, workspace bytes); unit_kind
+    PG_STAGE_PAGE (0) or PG_STAGE_ROW (1)."""
     u, m, w = _i64(), _i64(), _i64()
     _check("pg_stage_geometry", lib().pg_stage_geometry(
-        ctypes.byref(layout), table_dtype, int(n_tok), ctypes.byref(u), ctypes.byref(m),
-        ctypes.byref(w)))
+        ctypes.byref(layout), table_dtype, int(unit_kind), int(n_tok), ctypes.byref(u),
+        ctypes.byref(m), ctypes.byref(w)))
     return u.value, m.value, w.value
 
 
 def pg_stage_rows(layout, src, rows, cache, cache_rows, n_units, workspace, unit_first=None,
-                  stream=None):
+                  unit_kind=0, stream=None):
     """rows int64 [N, O, K] (device); src / cache pg_table structures."""
     _check("pg_stage_rows", lib().pg_stage_rows(
-        ctypes.byref(layout), ctypes.byref(src), _ptr(rows), rows.shape[0], ctypes.byref(cache),
+        ctypes.byref(layout), ctypes.byref(src), int(unit_kind), _ptr(rows), rows.shape[0],
+        ctypes.byref(cache),
         _ptr(cache_rows), _ptr(n_units), _ptr(unit_first), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 

@@ -331,11 +331,16 @@ namespace {
 
 // Rows per staging unit: a PageGram page, or the Engram-style tables'
 // 4 KiB run (row bytes: fp32 4r, bf16 2r, NF4 r/2 codes + 2 scale bytes).
-int64_t stage_unit_rows(const DevLayout& L, int32_t dt) {
+int64_t stage_unit_rows(const DevLayout& L, int32_t dt, int32_t unit_kind) {
+  if (unit_kind == PG_STAGE_ROW) return 1;
   if (L.kind == PG_PAGEGRAM) return (int64_t)L.K * (int64_t)L.S;
   const int64_t rb = dt == PG_F32 ? 4 * L.r : dt == PG_BF16 ? 2 * L.r : L.r / 2 + 2;
   const int64_t u = 4096 / rb;
   return u < 1 ? 1 : u;
+}
+
+int stage_share(const DevLayout& L, int32_t unit_kind) {
+  return L.kind == PG_PAGEGRAM && unit_kind == PG_STAGE_PAGE ? 1 : 0;
 }
 
 int64_t data_row_bytes(const DevLayout& L, int32_t dt) {
@@ -352,17 +357,19 @@ int check_cache(const DevLayout& L, const pg_table* t, int32_t dt) {
 
 }  // namespace
 
-PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64_t n_tok,
-                             int64_t* unit_rows, int64_t* max_units, int64_t* workspace_bytes) {
+PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int32_t unit_kind,
+                             int64_t n_tok, int64_t* unit_rows, int64_t* max_units,
+                             int64_t* workspace_bytes) {
   DevLayout L;
   int st = prepare_layout(layout, &L);
   if (st != PG_OK) return st;
   if (table_dtype != PG_F32 && table_dtype != PG_BF16 && table_dtype != PG_NF4) return PG_EINVAL;
+  if (unit_kind != PG_STAGE_PAGE && unit_kind != PG_STAGE_ROW) return PG_EINVAL;
   if (n_tok < 0) return PG_EINVAL;
   if (n_tok > kMaxTokens) return PG_ERANGE;
-  const int64_t U = stage_unit_rows(L, table_dtype);
-  if (U > INT_MAX) return PG_EUNSUPPORTED;
-  const pg::StagePlan p = pg::stage_plan(L, (int)U, n_tok);
+  const int64_t U = stage_unit_rows(L, table_dtype, unit_kind);
+  if (U > 65536) return PG_EUNSUPPORTED;
+  const pg::StagePlan p = pg::stage_plan(L, (int)U, stage_share(L, unit_kind), n_tok);
   if (p.H > ((int64_t)1 << 31)) return PG_ERANGE;
   if (unit_rows) *unit_rows = U;
   if (max_units) *max_units = p.max_units;
@@ -370,8 +377,9 @@ PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64
   return PG_OK;
 }
 
-PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, const int64_t* rows,
-                         int64_t n_tok, const pg_table* cache, int64_t* cache_rows,
+PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, int32_t unit_kind,
+                         const int64_t* rows, int64_t n_tok, const pg_table* cache,
+                         int64_t* cache_rows,
                          int64_t* n_units, int64_t* unit_first, void* workspace,
                          int64_t workspace_bytes, hipStream_t stream) {
   DevLayout L;
@@ -382,14 +390,14 @@ PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, const int
   st = check_cache(L, cache, src->dtype);
   if (st != PG_OK) return st;
   int64_t U = 0, max_units = 0, ws_bytes = 0;
-  st = pg_stage_geometry(layout, src->dtype, n_tok, &U, &max_units, &ws_bytes);
+  st = pg_stage_geometry(layout, src->dtype, unit_kind, n_tok, &U, &max_units, &ws_bytes);
   if (st != PG_OK) return st;
   if (!n_units) return PG_EINVAL;
   if (n_tok == 0) return hip_status(pg::launch_set_i64(n_units, 0, stream));
   if (!rows || !cache_rows) return PG_EINVAL;
   if (cache->n_rows < max_units * U) return PG_EINVAL;
   if (!workspace || workspace_bytes < ws_bytes || !aligned(workspace, 256)) return PG_EINVAL;
-  const pg::StagePlan p = pg::stage_plan(L, (int)U, n_tok);
+  const pg::StagePlan p = pg::stage_plan(L, (int)U, stage_share(L, unit_kind), n_tok);
   return hip_status(pg::launch_stage(L, p, (int)data_row_bytes(L, src->dtype), src->data,
                                      src->scales, rows, const_cast<void*>(cache->data),
                                      const_cast<void*>(cache->scales), cache_rows, n_units,

@@ -242,11 +242,12 @@ hipError_t launch_rms_flush(int64_t R, int r, float* table, float* vhat, int64_t
 // row in the data array (NF4: the r/2 code bytes; scales are separate).
 struct StagePlan {
   int U;
+  int share;        // the K heads of a token-order share a unit (PageGram pages)
   int64_t n_look, max_units, H, nb;
   int64_t off_keys, off_ranks, off_bcount, off_ufirst, off_ucount;
   int64_t bytes;
 };
-StagePlan stage_plan(const DevLayout& L, int U, int64_t n_tok);
+StagePlan stage_plan(const DevLayout& L, int U, int share, int64_t n_tok);
 hipError_t launch_stage(const DevLayout& L, const StagePlan& p, int rb, const void* src,
                         const void* src_scales, const int64_t* rows, void* dst,
                         void* dst_scales, int64_t* cache_rows, int64_t* n_units,

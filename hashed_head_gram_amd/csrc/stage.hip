@@ -3,19 +3,20 @@
 // Addresses are a pure function of the token IDs and are known before the
 // layer runs (PageGram tech report §3.3; Engram notes §3.5), so a table kept
 // in host memory can be fetched ahead: the units the step's lookups touch
-// are copied once into an HBM cache, and the gather reads the cache. A unit
-// is a PageGram page (K*S rows, shared by the K heads of a token-order) or,
-// for the Engram-style tables, a run of floor(4096 / row_bytes) rows of one
-// per-head table starting at the table's first row.
+// are copied once into an HBM cache, and the gather reads the cache. A page
+// unit is a PageGram page (K*S rows, shared by the K heads of a token-order)
+// or, for the Engram-style tables, a run of floor(4096 / row_bytes) rows of
+// one per-head table starting at the table's first row; a row unit is one
+// row.
 //
 //   clear    hash table keys <- empty
 //   insert   the unit (its first row) of each lookup, by linear probing
-//            (PageGram: one lookup per token-order: all K share the page)
+//            (PageGram pages: one lookup per token-order: all K share one)
 //   count / scan / rank
 //            slot of each occupied entry = its rank in table order
 //            (deterministic), unit lists by slot, the unit count
-//   copy     one block per unit: its rows (and NF4 scales) from the source
-//            table into cache slot s (rows s*U ..)
+//   copy     thread per (unit, 16-byte word): its rows (and NF4 scales)
+//            from the source table into cache slot s (rows s*U ..)
 //   remap    cache row of each lookup = slot * U + (row - first row)
 // Rows are clamped into the table, so a bad row cannot read outside it.
 #include "common.h"
@@ -34,6 +35,7 @@ __device__ __forceinline__ int64_t clamp_row(const DevLayout& L, int64_t row) {
 // First row of the unit holding `row` of head slot (i, k).
 __device__ __forceinline__ int64_t unit_first(const DevLayout& L, int U, int64_t row, int i,
                                               int k) {
+  if (U == 1) return row;
   if (L.kind == PG_PAGEGRAM) return (row / U) * U;
   const int64_t base = L.base_k[i * kMaxHeads + k];
   return base + ((row - base) / U) * U;
@@ -42,7 +44,7 @@ __device__ __forceinline__ int64_t unit_first(const DevLayout& L, int U, int64_t
 // Rows of the unit starting at f (the Engram-style tail unit of a table is
 // shorter).
 __device__ __forceinline__ int unit_count(const DevLayout& L, int U, int64_t f) {
-  if (L.kind == PG_PAGEGRAM) return U;
+  if (U == 1 || L.kind == PG_PAGEGRAM) return U;
   for (int i = 0; i < L.O; ++i)
     for (int k = 0; k < L.K; ++k) {
       const int hk = i * kMaxHeads + k;
@@ -59,14 +61,15 @@ __global__ __launch_bounds__(kThreads) void stage_clear_kernel(uint64_t* __restr
     keys[h] = kEmpty;
 }
 
+// share: the K heads of a token-order share one unit (PageGram pages).
 __global__ __launch_bounds__(kThreads) void stage_insert_kernel(
-    DevLayout L, int U, const int64_t* __restrict__ rows, int64_t n_look,
+    DevLayout L, int U, int share, const int64_t* __restrict__ rows, int64_t n_look,
     uint64_t* __restrict__ keys, uint32_t mask) {
   for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < n_look;
        q += (int64_t)gridDim.x * kThreads) {
     const int k = (int)(q % L.K);
     const int i = (int)((q / L.K) % L.O);
-    if (L.kind == PG_PAGEGRAM && k != 0) continue;
+    if (share && k != 0) continue;
     const uint64_t f = (uint64_t)unit_first(L, U, clamp_row(L, rows[q]), i, k);
     uint32_t h = (uint32_t)(mix64(f) & mask);
     for (uint32_t probe = 0; probe <= mask; ++probe) {   // the table is never full
@@ -162,24 +165,30 @@ __global__ __launch_bounds__(kThreads) void stage_rank_kernel(
   }
 }
 
-// Block per unit (grid-stride over slots): rows [f, f + count) of the source
-// -> cache rows [s U, s U + count); data rows are 16-byte multiples.
+// Thread per (unit s, 16-byte word w) over the staged units: rows
+// [f, f + count) of the source -> cache rows [s U, s U + count) (data rows
+// are 16-byte multiples); then thread per (unit, row) for NF4 scales.
 __global__ __launch_bounds__(kThreads) void stage_copy_kernel(
     const uint8_t* __restrict__ src, const __half* __restrict__ src_scales, int rb, int U,
     const int64_t* __restrict__ n_units, const int64_t* __restrict__ ufirst,
     const int32_t* __restrict__ ucount, uint8_t* __restrict__ dst,
     __half* __restrict__ dst_scales) {
   const int64_t nu = *n_units;
-  for (int64_t s = blockIdx.x; s < nu; s += gridDim.x) {
-    const int64_t f = ufirst[s];
-    const int cnt = ucount[s];
-    const uint4* a = reinterpret_cast<const uint4*>(src + f * rb);
-    uint4* b = reinterpret_cast<uint4*>(dst + s * U * (int64_t)rb);
-    const int words = cnt * rb / 16;
-    for (int w = threadIdx.x; w < words; w += kThreads) b[w] = a[w];
-    if (src_scales)
-      for (int w = threadIdx.x; w < cnt; w += kThreads) dst_scales[s * U + w] = src_scales[f + w];
+  const int wpu = U * rb / 16;                  // words of a full unit
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nu * wpu; g += stride) {
+    const int64_t s = g / wpu;
+    const int w = (int)(g - s * wpu);
+    if (w < ucount[s] * rb / 16)
+      reinterpret_cast<uint4*>(dst + s * U * (int64_t)rb)[w] =
+          reinterpret_cast<const uint4*>(src + ufirst[s] * rb)[w];
   }
+  if (src_scales)
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nu * U; g += stride) {
+      const int64_t s = g / U;
+      const int w = (int)(g - s * U);
+      if (w < ucount[s]) dst_scales[s * U + w] = src_scales[ufirst[s] + w];
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void stage_remap_kernel(
@@ -216,11 +225,12 @@ unsigned grid_for(int64_t n, int per_block) {
 
 }  // namespace
 
-StagePlan stage_plan(const DevLayout& L, int U, int64_t n_tok) {
+StagePlan stage_plan(const DevLayout& L, int U, int share, int64_t n_tok) {
   StagePlan p{};
   p.U = U;
+  p.share = share;
   p.n_look = n_tok * L.O * L.K;
-  p.max_units = L.kind == PG_PAGEGRAM ? n_tok * L.O : p.n_look;
+  p.max_units = share ? n_tok * L.O : p.n_look;
   int64_t H = 1024;
   while (H < 2 * p.max_units) H <<= 1;
   p.H = H;
@@ -250,13 +260,15 @@ hipError_t launch_stage(const DevLayout& L, const StagePlan& p, int rb, const vo
   hipLaunchKernelGGL(stage_clear_kernel, dim3(grid_for(p.H, kThreads)), dim3(kThreads), 0, s,
                      keys, p.H);
   hipLaunchKernelGGL(stage_insert_kernel, dim3(grid_for(p.n_look, kThreads)), dim3(kThreads), 0,
-                     s, L, p.U, rows, p.n_look, keys, mask);
+                     s, L, p.U, p.share, rows, p.n_look, keys, mask);
   hipLaunchKernelGGL(stage_count_kernel, dim3((unsigned)p.nb), dim3(kThreads), 0, s, keys, p.H,
                      bcount);
   hipLaunchKernelGGL(stage_scan_kernel, dim3(1), dim3(kThreads), 0, s, bcount, p.nb, n_units);
   hipLaunchKernelGGL(stage_rank_kernel, dim3((unsigned)p.nb), dim3(kThreads), 0, s, L, p.U, keys,
                      p.H, bcount, ranks, ufirst, ucount);
-  hipLaunchKernelGGL(stage_copy_kernel, dim3(grid_for(p.max_units, 1)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(stage_copy_kernel,
+                     dim3(grid_for(p.max_units * (int64_t)p.U * rb / 16, kThreads)),
+                     dim3(kThreads), 0, s,
                      static_cast<const uint8_t*>(src), static_cast<const __half*>(src_scales),
                      rb, p.U, n_units, ufirst, ucount, static_cast<uint8_t*>(dst),
                      static_cast<__half*>(dst_scales));

@@ -254,19 +254,22 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
  * table's first row (row_bytes: fp32 4r, bf16 2r, NF4 r/2 + 2).
  * ------------------------------------------------------------------------ */
 
+/* Unit of transfer: the page / 4 KiB run above, or single rows. */
+enum pg_stage_unit { PG_STAGE_PAGE = 0, PG_STAGE_ROW = 1 };
+
 /*
  * pg_stage_geometry -- rows per unit U, the most units a step of n_tok tokens
- * can touch (n_tok * orders for PageGram, n_tok * orders * K otherwise), and
- * the device workspace bytes of pg_stage_rows. Outputs are host pointers,
- * each nullable.
+ * can touch (n_tok * orders for PageGram pages, n_tok * orders * K
+ * otherwise), and the device workspace bytes of pg_stage_rows. Outputs are
+ * host pointers, each nullable.
  */
-PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64_t n_tok,
-                             int64_t* unit_rows, int64_t* max_units,
+PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int32_t unit_kind,
+                             int64_t n_tok, int64_t* unit_rows, int64_t* max_units,
                              int64_t* workspace_bytes);
 
 /*
- * pg_stage_rows -- copy every unit that rows touch, once, from src into a
- * device cache, and rewrite the rows for it.
+ * pg_stage_rows -- copy every unit (of kind unit_kind) that rows touch, once,
+ * from src into a device cache, and rewrite the rows for it.
  *   src         the whole table (pg_table as above); data (and NF4 scales)
  *               must be readable by the device: device memory, or pinned
  *               host memory allocated with hipHostMalloc
@@ -281,8 +284,9 @@ PG_API int pg_stage_geometry(const pg_layout* layout, int32_t table_dtype, int64
  *   workspace   pg_stage_geometry bytes of device memory, 256-byte aligned
  * Rows outside [0, R) are clamped into the table.
  */
-PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, const int64_t* rows,
-                         int64_t n_tok, const pg_table* cache, int64_t* cache_rows,
+PG_API int pg_stage_rows(const pg_layout* layout, const pg_table* src, int32_t unit_kind,
+                         const int64_t* rows, int64_t n_tok, const pg_table* cache,
+                         int64_t* cache_rows,
                          int64_t* n_units, int64_t* unit_first, void* workspace,
                          int64_t workspace_bytes, hipStream_t stream);
 

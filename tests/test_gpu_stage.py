@@ -59,15 +59,32 @@ def _as_bytes(t):
     return t.contiguous().view(torch.uint8).cpu().numpy()
 
 
+_cases = {}
+
+
+def case(name):
+    if name not in _cases:
+        _cases.clear()
+        c = Case(CASES[name])
+        _cases[name] = (c, _host_table(c))
+    return _cases[name]
+
+
+def teardown_module(module):
+    _cases.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["page", "row"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_staged_gather_equals_table_gather(name):
+def test_staged_gather_equals_table_gather(name, kind):
     wl = CASES[name]
-    print(f"[stage] {name}", flush=True)
-    c = Case(wl)
+    print(f"[stage] {name} {kind} units", flush=True)
+    c, (src, host) = case(name)
     dt = PG_DT[wl["table_dtype"]]
-    src, host = _host_table(c)
-    U, max_units, wsb = pg.pg_stage_geometry(c.layout, dt, c.N)
-    assert U == stage.unit_rows(c.lay_d, wl["table_dtype"])
+    uk = pg.PG_STAGE_PAGE if kind == "page" else pg.PG_STAGE_ROW
+    U, max_units, wsb = pg.pg_stage_geometry(c.layout, dt, c.N, unit_kind=uk)
+    assert U == stage.unit_rows(c.lay_d, wl["table_dtype"], kind)
     cache, cache_t = _cache(c, max_units * U)
     idx = c.run_index()
     rows, signs = idx["rows"], idx["signs"]
@@ -75,7 +92,8 @@ def test_staged_gather_equals_table_gather(name):
     n_units = torch.zeros(1, dtype=torch.int64, device=c.dev)
     unit_first = torch.full((max_units,), -1, dtype=torch.int64, device=c.dev)
     ws = torch.empty(wsb, dtype=torch.uint8, device=c.dev)
-    pg.pg_stage_rows(c.layout, src, rows, cache, cache_rows, n_units, ws, unit_first=unit_first)
+    pg.pg_stage_rows(c.layout, src, rows, cache, cache_rows, n_units, ws, unit_first=unit_first,
+                     unit_kind=uk)
     e = c.e_buffer()
     pg.pg_gather_staged(c.layout, cache, cache_rows, signs, c.e_dtype, e)
     e_ref = c.run_index_gather()
@@ -83,7 +101,7 @@ def test_staged_gather_equals_table_gather(name):
     assert torch.equal(e.view(torch.uint8), e_ref.view(torch.uint8))
     # units against the oracle
     rows_np = rows.cpu().numpy()
-    want_first, want_count = stage.staged_units(c.lay_d, wl["table_dtype"], rows_np)
+    want_first, want_count = stage.staged_units(c.lay_d, wl["table_dtype"], rows_np, kind)
     n = int(n_units.item())
     assert n == len(want_first)
     got_first = unit_first[:n].cpu().numpy()

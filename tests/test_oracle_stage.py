@@ -80,3 +80,14 @@ def test_units_partition_a_small_table():
     uf, uc = np.unique(f, return_index=True)
     assert int(c[uc].sum()) == R
     assert stage.staged_bytes(lay, "bf16", full[:, :, :]) >= R * 128
+
+
+@pytest.mark.parametrize("i", [1, 2])
+def test_row_units_are_the_distinct_rows(i):
+    wl = configs.workload(i)
+    rows = _rows(wl)
+    f, c = stage.staged_units(wl["layout"], wl["table_dtype"], rows, kind="row")
+    assert np.array_equal(f, np.unique(rows)) and (c == 1).all()
+    assert stage.staged_bytes(wl["layout"], wl["table_dtype"], rows, kind="row") == \
+        len(np.unique(rows)) * 2 * wl["layout"]["r"]
+
