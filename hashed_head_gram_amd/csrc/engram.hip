@@ -25,6 +25,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTB = 32;          // tokens per block
 constexpr int kCB = 256;         // channels per block
+constexpr int kMaxBranches = 8;  // largest M (validated by the caller)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32); a low.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Eight bf16 (16 bytes, element 0 in the low half of the first word) to fp32.
+__device__ __forceinline__ void unpack8(uint4 raw, float (&v)[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    v[2 * x] = __uint_as_float(w[x] << 16);
+    v[2 * x + 1] = __uint_as_float(w[x] & 0xFFFF0000u);
+  }
+}
 constexpr int kColBlock = 256;   // pass-1 column block of the partial sums
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -103,65 +123,54 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
   const int cg = tid & 31;
   const int c = c0 + cg * 8;
   if (c >= d) return;
-  float w[8][kw];
-  float gu[8];
+  // conv weights with the RMSNorm_u gain folded in: wg = w * gamma_u
+  float wg[8][kw];
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
-    gu[x] = gamma_u[c + x];
+    const float gu = gamma_u[c + x];
 #pragma unroll
-    for (int j = 0; j < kw; ++j) w[x][j] = conv_w[(c + x) * kw + j];
+    for (int j = 0; j < kw; ++j) wg[x][j] = conv_w[(c + x) * kw + j] * gu;
   }
   for (int tl = tid >> 5; tl < kTB; tl += kThreads / 32) {
     const int64_t t = t0 + tl;
     if (t >= T) break;
     const int li = tl + H;  // LDS index of t
     float vc[8];
-    {
-      const uint4 raw = *reinterpret_cast<const uint4*>(&vt[li * kCB + cg * 8]);
-      const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
+    unpack8(*reinterpret_cast<const uint4*>(&vt[li * kCB + cg * 8]), vc);
+    // the kw taps' v values (shared by the branches)
+    float vj[kw][8];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        vc[2 * x] = bf16_to_f32((uint16_t)(ws[x] & 0xFFFFu));
-        vc[2 * x + 1] = bf16_to_f32((uint16_t)(ws[x] >> 16));
-      }
-    }
-    for (int m = 0; m < Mbr; ++m) {
+    for (int j = 0; j < kw; ++j)
+      unpack8(*reinterpret_cast<const uint4*>(&vt[(li - (kw - 1 - j) * dil) * kCB + cg * 8]),
+              vj[j]);
+#pragma unroll
+    for (int m = 0; m < kMaxBranches; ++m) {
+      if (m >= Mbr) break;
+      // the residual load goes out before the conv arithmetic
+      const uint4 hr = add_resid ? *reinterpret_cast<const uint4*>(
+                                       h + (((int64_t)m * N + b * T + t) * d + c))
+                                 : make_uint4(0, 0, 0, 0);
       float conv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kw; ++j) {
-        const int lj = li - (kw - 1 - j) * dil;   // >= 0; zero rows before the start
-        const float f = facS[m * rowsL + lj];
-        const uint4 raw = *reinterpret_cast<const uint4*>(&vt[lj * kCB + cg * 8]);
-        const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float f = facS[m * rowsL + li - (kw - 1 - j) * dil];   // 0 before the start
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          conv[2 * x] += w[2 * x][j] * (gu[2 * x] * bf16_to_f32((uint16_t)(ws[x] & 0xFFFFu)) * f);
-          conv[2 * x + 1] +=
-              w[2 * x + 1][j] * (gu[2 * x + 1] * bf16_to_f32((uint16_t)(ws[x] >> 16)) * f);
-        }
+        for (int x = 0; x < 8; ++x) conv[x] += wg[x][j] * (vj[j][x] * f);
       }
       const float alpha = alphaS[m * rowsL + li];
-      const int64_t o = ((int64_t)m * N + b * T + t) * d + c;
-      float hv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (add_resid) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(h + o);
-        const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          hv[2 * x] = bf16_to_f32((uint16_t)(ws[x] & 0xFFFFu));
-          hv[2 * x + 1] = bf16_to_f32((uint16_t)(ws[x] >> 16));
-        }
-      }
+      float hv[8];
+      unpack8(hr, hv);
       uint32_t res[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        float y0 = conv[2 * x], y1 = conv[2 * x + 1];
-        y0 = y0 / (1.0f + expf(-y0));
-        y1 = y1 / (1.0f + expf(-y1));
-        const float o0 = hv[2 * x] + (alpha * vc[2 * x] + y0);
-        const float o1 = hv[2 * x + 1] + (alpha * vc[2 * x + 1] + y1);
-        res[x] = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+        // SiLU(y) = y / (1 + e^-y)
+        const float y0 = conv[2 * x] * __builtin_amdgcn_rcpf(1.0f + __expf(-conv[2 * x]));
+        const float y1 =
+            conv[2 * x + 1] * __builtin_amdgcn_rcpf(1.0f + __expf(-conv[2 * x + 1]));
+        res[x] = pack_bf16x2(hv[2 * x] + (alpha * vc[2 * x] + y0),
+                             hv[2 * x + 1] + (alpha * vc[2 * x + 1] + y1));
       }
+      const int64_t o = ((int64_t)m * N + b * T + t) * d + c;
       *reinterpret_cast<uint4*>(out + o) = make_uint4(res[0], res[1], res[2], res[3]);
     }
   }
