@@ -111,6 +111,7 @@ def source_digest(paths):
 KERNEL_SOURCES = {
     "gather": ["hashed_head_gram_amd/csrc/index.hip", "hashed_head_gram_amd/csrc/common.h"],
     "projection": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
+    "gathered": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
 }
 
 
@@ -130,7 +131,7 @@ def traffic_for(stage, workload):
 
 COPY_BYTES = 1 << 30
 TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_kernel",
-                   "copy": "copyBuffer"}
+                   "gathered": "gemm_pipe_gather_kernel", "copy": "copyBuffer"}
 
 
 def counter_means(path, counter):
@@ -152,7 +153,8 @@ def counter_means(path, counter):
 
 
 def write_traffic(workload, fetch_csv, write_csv):
-    """HBM bytes per launch of the gather and projection kernels: FETCH_SIZE and
+    """HBM bytes per launch of the gather and projection kernels (and of the
+    gathered projection where the workload runs it): FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
     1 GiB device copy read and write exactly 1 GiB."""
     fetch = counter_means(fetch_csv, "FETCH_SIZE")
@@ -162,7 +164,9 @@ def write_traffic(workload, fetch_csv, write_csv):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
-    for stage in ("gather", "projection"):
+    for stage in ("gather", "projection", "gathered"):
+        if stage not in fetch or stage not in write:
+            continue
         rd = fetch[stage] * 1024 * f_scale
         wr = write[stage] * 1024 * w_scale
         ent[stage] = {"kernel": TRAFFIC_KERNELS[stage],
@@ -662,16 +666,36 @@ def main():
 
         def project_call(j):
             pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws2)
+    # pg_forward runs as pg_index_records -> pg_project_gathered (E gathered
+    # inside the matrix kernel) for bf16 tables of 64-element rows under the
+    # scalar gate; otherwise as pg_index_gather -> pg_project_gate.
+    gathered = (not fp8 and wl["table_dtype"] == "bf16" and r == 64
+                and wl["gate"] == "scalar")
+    if gathered:
+        rec = torch.empty(pg.records_bytes(layout, N), dtype=torch.uint8, device=dev)
+
+        def records_call(j):
+            pg.pg_index_records(layout, pool[j % POOL], cmap, rec)
+
+        def gathered_call(j):
+            pg.pg_project_gathered(layout, table, fuse, rec, B, T, W, resid, out)
     torch.cuda.synchronize()
 
     # The stage calls reproduce pg_forward bit for bit.
     out_fwd = torch.empty_like(out)
     forward(0)
     out_fwd.copy_(out)
+    if gathered:
+        records_call(0)
+        gathered_call(0)
+        torch.cuda.synchronize()
+        same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
     gather_call(0)
     project_call(0)
     torch.cuda.synchronize()
-    same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
+    same_two_stage = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
+    if not gathered:
+        same = same_two_stage
     del out_fwd
 
     for j in range(args.warmup):
@@ -701,6 +725,7 @@ def main():
         return a.elapsed_time(b) / args.steps
     g_ms = np.array([per_launch_ms(gather_call)])
     p_ms = np.array([per_launch_ms(project_call)])
+    gp_ms = np.array([per_launch_ms(gathered_call)]) if gathered else None
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -733,7 +758,28 @@ def main():
     sfx = "_fp8" if fp8 else ""
     stages = {f"pg_index_gather{sfx}_ms": float(g_ms.mean()),
               f"pg_project_gate{sfx}_ms": float(p_ms.mean())}
-    if g_ms.mean() >= p_ms.mean():
+    gathered_rec = None
+    if gathered:
+        # the matrix kernel reads each token's 2K table rows and records
+        # (16 B per head slot) besides x and out
+        OK = costs["E"] // r
+        gp_bytes = (costs["proj_bytes"] - E * 2 + OK * (2 * r + 16)) * N
+        gp_tflops = p_flops / (gp_ms.mean() / 1e3) / 1e12
+        gathered_rec = {
+            "kernel": "gemm_pipe_gather_kernel", "ms_mean": float(gp_ms.mean()),
+            "flops_per_launch": p_flops, "achieved_TFLOPs": gp_tflops,
+            "frac_mfma_peak": gp_tflops / p_peak, "bytes_per_launch": gp_bytes,
+            "achieved_GBps": gp_bytes / (gp_ms.mean() / 1e3) / 1e9,
+            "traffic": traffic_for("gathered", tkey),
+            # records_kernel: the rest of a step (K launches of the pair take
+            # step_ms_gpu_events each)
+            "records_kernel_ms_derived": step_gpu_ms - float(gp_ms.mean()),
+            "records_bytes_per_launch": N * (4 + 16 * OK)}
+        stages["pg_project_gathered_ms"] = float(gp_ms.mean())
+        roof = {"kernel": gathered_rec["kernel"], "bound": "mfma", "achieved": gp_tflops,
+                "peak": p_peak, "unit": "TFLOP/s", "frac": gp_tflops / p_peak,
+                "traffic": gathered_rec["traffic"]}
+    elif g_ms.mean() >= p_ms.mean():
         roof = {"kernel": gather_rec["kernel"], "bound": "hbm", "achieved": g_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
                 "traffic": gather_rec["traffic"]}
@@ -759,9 +805,13 @@ def main():
         "roofline": roof,
         "step_ms_gpu_events": step_gpu_ms,
         "stages": stages,
+        "forward_path": ("pg_index_records -> pg_project_gathered" if gathered else
+                         "pg_index_gather -> pg_project_gate"),
+        "gathered_projection": gathered_rec,
         "gather": gather_rec,
         "projection": proj,
         "forward_matches_stage_calls": bool(same),
+        "forward_matches_two_stage": bool(same_two_stage),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -58,6 +58,9 @@ _SIGS = {
                                _vp, _i64, _vp]),
     "pg_forward": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                           _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pg_index_records": (_i32, [_P(PgLayout), _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "pg_project_gathered": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
+                                   _vp, _vp, _vp, _vp]),
     "pg_stage_geometry": (_i32, [_P(PgLayout), _i32, _i32, _i64, _P(_i64), _P(_i64),
                                  _P(_i64)]),
     "pg_stage_rows": (_i32, [_P(PgLayout), _P(PgTable), _i32, _vp, _i64, _P(PgTable), _vp, _vp,
@@ -236,6 +239,24 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+def records_bytes(layout, n_tok):
+    """Bytes of pg_index_records' output: 16 per (head slot, token)."""
+    return 16 * n_tok * (layout.n_max - layout.n_min + 1) * layout.K
+
+
+def pg_index_records(layout, tokens, canon_map, rec_out, dev_status=None, stream=None):
+    B, T = tokens.shape
+    _check("pg_index_records", lib().pg_index_records(
+        ctypes.byref(layout), _ptr(tokens), B, T, _ptr(canon_map), canon_map.numel(),
+        _ptr(rec_out), _ptr(dev_status), _stream(stream)))
+
+
+def pg_project_gathered(layout, table, fuse, rec, B, T, W, resid, out, stream=None):
+    _check("pg_project_gathered", lib().pg_project_gathered(
+        ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(rec), int(B),
+        int(T), _ptr(W), _ptr(resid), _ptr(out), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -135,6 +135,20 @@ int64_t project_workspace(const pg_fuse* f, int64_t N) {
 
 int64_t elt_bytes(int32_t dt) { return dt == PG_F32 ? 4 : 2; }
 
+// Records of the gathered projection: 64-element rows (one sign word per
+// head), 32-bit record offsets within a head slot.
+constexpr int64_t kMaxRecordTokens = (int64_t)1 << 28;
+bool records_ok(const DevLayout& L, int64_t N) {
+  return L.r == 64 && L.W == 1 && N <= kMaxRecordTokens;
+}
+
+// The gathered projection: bf16 tables of 64-element rows whose byte
+// offsets fit 32 bits, under the scalar gate.
+bool gathered_ok(const DevLayout& L, const pg_table* t, const pg_fuse* f, int64_t N) {
+  return records_ok(L, N) && t->dtype == PG_BF16 && f->gate == PG_GATE_SCALAR &&
+         L.n_rows <= ((int64_t)1 << 25);
+}
+
 // Projection + fusion on an e already in device memory.
 int run_project(const pg_fuse* f, const void* e, int64_t B, int64_t T, int64_t e_dim,
                 const void* W, const void* resid, void* out, void* ws, hipStream_t s) {
@@ -316,12 +330,62 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
   const int64_t e_bytes = align256(N * e_dim * elt_bytes(fuse->dtype));
   const int64_t need = e_bytes + project_workspace(fuse, N);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PG_EINVAL;
+  // bf16 table rows of 64 elements under the scalar gate: the projection
+  // gathers its E operand from the table itself, by per-(head slot, token)
+  // records of row and signs (same products, same order); the records take
+  // N (O K) 16 bytes of the workspace
+  if (gathered_ok(L, table, fuse, N)) {
+    const void* x = fuse->increment_only ? nullptr : resid;
+    st = hip_status(pg::launch_records(L, tokens, B, T, canon_map, V, workspace, dev_status,
+                                       stream));
+    if (st != PG_OK) return st;
+    return hip_status(pg::launch_project_gathered(table->data, workspace, N, e_dim, W, fuse->d,
+                                                  fuse->g, x, out, stream));
+  }
   void* e = workspace;
   void* ws = static_cast<uint8_t*>(workspace) + e_bytes;
   st = hip_status(pg::launch_index_gather(L, table->dtype, table->data, table->scales, tokens,
                                           B, T, canon_map, V, e, dev_status, 0, 0, stream));
   if (st != PG_OK) return st;
   return run_project(fuse, e, B, T, e_dim, W, resid, out, ws, stream);
+}
+
+PG_API int pg_index_records(const pg_layout* layout, const int32_t* tokens, int64_t B,
+                            int64_t T, const int32_t* canon_map, int64_t V, void* rec_out,
+                            int32_t* dev_status, hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_tokens(tokens, B, T, canon_map, V);
+  if (st != PG_OK) return st;
+  if (!records_ok(L, B * T)) return L.r != 64 ? PG_EUNSUPPORTED : PG_ERANGE;
+  if (B * T == 0) return PG_OK;
+  if (!rec_out || !aligned(rec_out, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_records(L, tokens, B, T, canon_map, V, rec_out, dev_status,
+                                       stream));
+}
+
+PG_API int pg_project_gathered(const pg_layout* layout, const pg_table* table,
+                               const pg_fuse* fuse, const void* rec, int64_t B, int64_t T,
+                               const void* W, const void* resid, void* out,
+                               hipStream_t stream) {
+  DevLayout L;
+  int st = prepare_layout(layout, &L);
+  if (st != PG_OK) return st;
+  st = check_table(L, table);
+  if (st != PG_OK) return st;
+  const int64_t e_dim = (int64_t)L.O * L.K * L.r;
+  st = check_fuse(fuse, B, T, e_dim);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (fuse->dtype != PG_BF16 || !gathered_ok(L, table, fuse, N)) return PG_EUNSUPPORTED;
+  if (N == 0) return PG_OK;
+  if (!rec || !W || !out || !aligned(rec, 16) || !aligned(W, 16) || !aligned(out, 16))
+    return PG_EINVAL;
+  if (resid && !aligned(resid, 16)) return PG_EINVAL;
+  const void* x = fuse->increment_only ? nullptr : resid;
+  return hip_status(pg::launch_project_gathered(table->data, rec, N, e_dim, W, fuse->d, fuse->g,
+                                                x, out, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -202,6 +202,19 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
                                  const void* W, int64_t d, float g, const void* resid,
                                  void* out, hipStream_t s);
 
+// pg_forward's fused path for bf16 tables of 64-element rows under the
+// scalar gate. launch_records writes, for head slot hs = i K + k and token
+// t, rec[hs][t] = {row, the sign bits of the two MFMA lane halves, 0}
+// (4 x uint32; B T (O K) 16 bytes); launch_project_gathered is the
+// scalar-gate projection with its E operand (E = 64 O K) gathered from the
+// table by those records.
+hipError_t launch_records(const DevLayout& L, const int32_t* tokens, int64_t B, int64_t T,
+                          const int32_t* cmap, int64_t V, void* rec, int32_t* status,
+                          hipStream_t s);
+hipError_t launch_project_gathered(const void* table, const void* rec, int64_t N, int64_t E,
+                                  const void* W, int64_t d, float g, const void* resid,
+                                  void* out, hipStream_t s);
+
 // The same on E4M3 operands e8 = E4M3(e 2^se), W8 = E4M3(W 2^sw).
 hipError_t launch_project_scalar_fp8(const void* e8, int64_t N, int64_t E, const void* W8,
                                      int64_t d, float g, const void* resid, void* out,

@@ -196,16 +196,29 @@ struct PipeCfg {
   static constexpr int kLdsBytes = kRingBytes > kStageTileBytes ? kRingBytes : kStageTileBytes;
 };
 
+// Fused gather (pg_forward with a bf16 table of 64-element rows): the E tile
+// of K stage kt is head slot kt of the tile's tokens, so its rows are table
+// rows, loaded straight into the ring from the table. A token-order's page
+// is hashed once per tile; the first BM lanes hash the heads (and sign
+// words) of stage kt + 3 while stage kt is multiplied. The +-1 signs are
+// applied to the E fragments after the LDS read, with 16-byte XOR masks
+// looked up by sign byte in an LDS table.
+struct GatherArgs {
+  const uint8_t* table;        // [R][64] bf16 rows (R * 128 bytes < 2^32)
+  const uint8_t* rec;          // [K / 64][M] records {row, sign words of the two
+                               // lane halves, 0}
+};
+
 // WGM x WGN waves (64 WGM WGN threads): 2 x 2 puts one wave on each SIMD;
 // 2 x 4 and 4 x 2 put two, so one wave's matrix work covers the other's
 // barrier and LDS waits. F8: E4M3 operands (BK = 128 K elements per stage)
 // on v_mfma_scale_f32_32x32x64_f8f6f4, whose E8M0 operand scales undo the
 // operands' power-of-two scaling; otherwise bf16 (BK = 64) on
 // v_mfma_f32_32x32x16_bf16. Either way a row's K stage is 128 bytes.
-template <int BM, int BN, int BK, int S, int EPI, int MINB, int WGM, int WGN, bool F8>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bw, int64_t M, int N,
-    int K, EpiArgs ep) {
+template <int BM, int BN, int BK, int S, int EPI, int WGM, int WGN, bool F8, bool GATHER>
+__device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
+                                          const uint8_t* __restrict__ Bw, int64_t M, int N,
+                                          int K, const EpiArgs& ep, const GatherArgs& ga) {
   constexpr int EB = F8 ? 1 : 2;                // operand element bytes
   constexpr int BKB = BK * EB;                  // bytes of a row's K stage
   using Cfg = PipeCfg<BM, BN, BKB, S>;
@@ -227,8 +240,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
   static_assert(L < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
   static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
+  static_assert(!GATHER || (!F8 && BKB == 128 && EPI == EPI_SCALAR && S == 2 && NT >= BM),
+                "fused gather: bf16 64-element rows, scalar gate");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLdsBytes];
+  // fused gather: the records of four head slots (rows and sign words of
+  // the tile's tokens)
+  __shared__ __attribute__((aligned(16))) uint4 recL[GATHER ? 4 : 1][GATHER ? BM : 1];
 
   const int64_t lda = ep.lda ? ep.lda : K;
   const int64_t ldb = ep.ldb ? ep.ldb : K;
@@ -306,14 +324,36 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
   auto issue_a = [&](int kt) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j)
-      issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, wave * A_DMA + j, kt, la + j * 1024);
+    for (int j = 0; j < A_DMA; ++j) {
+      if constexpr (GATHER) {
+        // lane's row: table row of head slot kt of token row grp * RPI + dr
+        const int grp = wave * A_DMA + j;
+        const uint32_t row = recL[kt % 4][grp * RPI + dr].x;
+        dma16(ga.table, row * 128u + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)),
+              la + j * 1024);
+      } else {
+        issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, wave * A_DMA + j, kt,
+                   la + j * 1024);
+      }
+    }
   };
   auto issue_b = [&](int kt) {
     const uint32_t lb = lds0 + Cfg::kBOffset + (kt % S) * Cfg::kBBytes + wave * B_DMA * 1024;
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j)
       issue_rows(Bw, ldb, N, n0 + (wave * B_DMA + j) * RPI, wave * B_DMA + j, kt, lb + j * 1024);
+  };
+  // fused gather: DMA of head slot hs's records for the tile's tokens into
+  // buffer hs % 4, by the first BM / 64 waves (tokens past M repeat the
+  // last token's record)
+  auto issue_rec = [&](int hs) {
+    if constexpr (GATHER) {
+      if (wave * 64 < BM) {
+        const int64_t tok = m0 + wave * 64 + lane;
+        const uint32_t off = (uint32_t)((tok < M ? tok : M - 1) * 16);
+        dma16(ga.rec + (int64_t)hs * M * 16, off, lds_addr(&recL[hs % 4][wave * 64]));
+      }
+    }
   };
 
   f32x16_t acc[FM][FN];
@@ -388,6 +428,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
   constexpr int RD = (FM + FN) * CPF;           // LDS reads per step
   constexpr int NMF = FM * FN;                  // MFMAs per step
   constexpr int RPM = (RD + NMF - 1) / NMF;     // reads issued after each MFMA
+  if constexpr (GATHER) {
+    issue_rec(0);
+    if (KT > 1) issue_rec(1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
 #pragma unroll
   for (int st = 0; st < PD; ++st)
     if (st < KT) {
@@ -406,16 +452,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
       wait_vmcnt<0>();
     block_sync();
     // the stage that reuses the buffers of stage kt-1 goes out at once, so
-    // its load latency overlaps this stage's whole matrix work
+    // its load latency overlaps this stage's whole matrix work (fused
+    // gather: after the records of head slot kt + 2, one stage ahead of its
+    // rows; the ring is then one stage deep, so the wait at the top of the
+    // next step covers both)
+    if (GATHER && kt + 2 < KT) issue_rec(kt + 2);
     if (kt + PD < KT) {
       issue_b(kt + PD);
       issue_a(kt + PD);
     }
+    // fused gather: this lane half's sign words of the stage's E rows
+    uint32_t sgn[FM];
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint4 r = recL[kt % 4][wm * WTM + i * 32 + fr];
+        sgn[i] = lane < 32 ? r.y : r.z;
+      }
+    }
+    // the bf16 sign bits (15 and 31) of dword q of K step st's fragment are
+    // flipped by bits 15 - s and 31 - s of the sign word, s = 4 st + q
+    auto apply_signs = [&](int st, frag_t (&af)[FM]) {
+      if constexpr (GATHER) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          uint4 v = __builtin_bit_cast(uint4, af[i]);
+          v.x ^= (sgn[i] << (4 * st)) & 0x80008000u;
+          v.y ^= (sgn[i] << (4 * st + 1)) & 0x80008000u;
+          v.z ^= (sgn[i] << (4 * st + 2)) & 0x80008000u;
+          v.w ^= (sgn[i] << (4 * st + 3)) & 0x80008000u;
+          af[i] = __builtin_bit_cast(frag_t, v);
+        }
+      }
+    };
     frag_t fa[NS][FM], fb[NS][FN];
     load_frags(kt, 0, fa[0], fb[0]);
+    apply_signs(0, fa[0]);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      if (st + 1 < NS) load_frags(kt, st + 1, fa[st + 1], fb[st + 1]);
+      if (st + 1 < NS) {
+        load_frags(kt, st + 1, fa[st + 1], fb[st + 1]);
+        apply_signs(st + 1, fa[st + 1]);
+      }
       mma(fa[st], fb[st]);
       if (st == 0) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
       if (st + 1 < NS) {
@@ -652,6 +730,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
   }
 }
 
+template <int BM, int BN, int BK, int S, int EPI, int MINB, int WGM, int WGN, bool F8>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_pipe_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bw, int64_t M, int N,
+    int K, EpiArgs ep) {
+  const GatherArgs none{};
+  pipe_body<BM, BN, BK, S, EPI, WGM, WGN, F8, false>(A, Bw, M, N, K, ep, none);
+}
+
+// pg_forward's fused path: the E operand gathered from the table.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_pipe_gather_kernel(
+    const uint8_t* __restrict__ Bw, int64_t M, int N, int K, EpiArgs ep, GatherArgs ga) {
+  pipe_body<BM, BN, 64, 2, EPI_SCALAR, WGM, WGN, false, true>(nullptr, Bw, M, N, K, ep, ga);
+}
+
 // ---------------------------------------------------------------------------
 // Fallback kernel (K % 8 == 0), scalar gate
 
@@ -846,6 +939,35 @@ hipError_t launch_project_scalar(int32_t dtype, const void* e, int64_t N, int64_
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(W), N,
                      (int)d, (int)E, ep);
+  return hipGetLastError();
+}
+
+// pg_forward's fused path (bf16 table with r = 64, scalar gate; checked by
+// the caller): out[N][d] = resid + g * e W^T with e gathered in the kernel.
+hipError_t launch_project_gathered(const void* table, const void* rec, int64_t N, int64_t E,
+                                  const void* W, int64_t d, float g, const void* resid,
+                                  void* out, hipStream_t s) {
+  EpiArgs ep{};
+  ep.g = g;
+  ep.resid = static_cast<const uint16_t*>(resid);
+  ep.out = static_cast<uint16_t*>(out);
+  GatherArgs ga{};
+  ga.table = static_cast<const uint8_t*>(table);
+  ga.rec = static_cast<const uint8_t*>(rec);
+  const auto* Wb = static_cast<const uint8_t*>(W);
+  auto cost = [&](int64_t bn) {
+    const int64_t blocks = ((N + 255) / 256) * ((d + bn - 1) / bn);
+    return ((blocks + 255) / 256) * bn;
+  };
+  if (cost(192) < cost(256)) {
+    const int64_t blocks = ((N + 255) / 256) * ((d + 191) / 192);
+    hipLaunchKernelGGL((gemm_pipe_gather_kernel<256, 192, 4, 2>), dim3((unsigned)blocks),
+                       dim3(512), 0, s, Wb, N, (int)d, E, ep, ga);
+  } else {
+    const int64_t blocks = ((N + 255) / 256) * ((d + 255) / 256);
+    hipLaunchKernelGGL((gemm_pipe_gather_kernel<256, 256, 2, 4>), dim3((unsigned)blocks),
+                       dim3(512), 0, s, Wb, N, (int)d, E, ep, ga);
+  }
   return hipGetLastError();
 }
 

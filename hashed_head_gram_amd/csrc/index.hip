@@ -230,6 +230,79 @@ __global__ __launch_bounds__(kThreads) void index_kernel(
     signs_out[gid * L.W + w] = sign_word(L, rc, g, i, k, w);
 }
 
+// Records of the fused projection (64-element rows, one sign word). A block
+// takes kRecTok tokens: their canonical IDs (and the H = n_max - 1 before
+// them) are staged in LDS once, the token loads going out before the role
+// constants are derived; thread (hs, token) then hashes one head slot and
+// stores its record (threads loop over the (hs, token) pairs), slot-major
+// so each slot's records are contiguous.
+constexpr int kRecTok = 16;
+
+// Sign bits of the fused projection's fragments: a lane of half h holds
+// elements 16 st + 8 h + x (x < 8) of a 64-element row in K step st, as
+// four dwords whose bits 15 and 31 are the signs of elements x = 2q and
+// 2q + 1 of dword q. The word for half h puts the sign of element
+// 16 st + 8 h + 2q at bit 15 - s and that of 2q + 1 at bit 31 - s, with
+// s = 4 st + q, so dword q's XOR mask is (word << s) & 0x80008000.
+__device__ __forceinline__ uint32_t sign_lane_word(uint64_t sw, int h) {
+  // bytes 2 st + h of the word (the half's eight elements of each step)
+  uint32_t x = __builtin_amdgcn_perm((uint32_t)(sw >> 32), (uint32_t)sw,
+                                     h ? 0x07050301u : 0x06040200u);
+  // bit unshuffle: the even bits (elements 2q) to bits 0-15, the odd ones
+  // (2q + 1) to bits 16-31, each in (st, q) order
+  uint32_t t = (x ^ (x >> 1)) & 0x22222222u;
+  x ^= t ^ (t << 1);
+  t = (x ^ (x >> 2)) & 0x0C0C0C0Cu;
+  x ^= t ^ (t << 2);
+  t = (x ^ (x >> 4)) & 0x00F000F0u;
+  x ^= t ^ (t << 4);
+  t = (x ^ (x >> 8)) & 0x0000FF00u;
+  x ^= t ^ (t << 8);
+  // swap the halves and reverse: (st, q) = s lands at 15 - s (odd: 31 - s)
+  return __builtin_bitreverse32((x << 16) | (x >> 16));
+}
+
+__global__ __launch_bounds__(kThreads) void records_kernel(
+    DevLayout L, const int32_t* __restrict__ tokens, int64_t B, int64_t T,
+    const int32_t* __restrict__ cmap, int64_t V, uint4* __restrict__ rec,
+    int32_t* __restrict__ status) {
+  __shared__ uint64_t rc[kMaxRoles * kRoleStride];
+  __shared__ uint32_t canonL[kRecTok + kMaxOrders];
+  const int64_t N = B * T;
+  const int64_t tok0 = (int64_t)blockIdx.x * kRecTok;
+  const int tid = threadIdx.x;
+  const int H = L.n_min + L.O - 2;
+  const int64_t gt = tok0 - H + tid;
+  const bool have = tid < kRecTok + H && gt >= 0 && gt < N;
+  const int32_t tk = have ? tokens[gt] : 0;
+  load_role_consts(L, rc);                      // ends with a barrier
+  if (tid < kRecTok + H) {
+    const bool ok = have && tk >= 0 && (int64_t)tk < V;
+    canonL[tid] = ok ? (uint32_t)cmap[tk] : (uint32_t)L.pad_id;
+    if (status && have && tid >= H && !ok) atomicOr(status, 1);
+  }
+  __syncthreads();
+  for (int q = tid; q < L.O * L.K * kRecTok; q += kThreads) {
+    const int hs = q / kRecTok;
+    const int tl = q - hs * kRecTok;
+    const int64_t tok = tok0 + tl;
+    if (tok >= N) continue;
+    const int i = hs / L.K;
+    const int k = hs - i * L.K;
+    const int64_t t = tok % T;
+    const int n = L.n_min + i;
+    uint32_t g[kMaxOrders];
+#pragma unroll
+    for (int j = 0; j < kMaxOrders; ++j)
+      g[j] = j < n ? (t - j >= 0 ? canonL[H + tl - j] : (uint32_t)L.pad_id) : 0u;
+    uint64_t bh, u;
+    int64_t page;
+    const int64_t row = head_row(L, rc, g, i, k, &bh, &u, &page);
+    const uint64_t sw = sign_word(L, rc, g, i, k, 0);
+    rec[hs * N + tok] = make_uint4((uint32_t)row, sign_lane_word(sw, 0), sign_lane_word(sw, 1), 0u);
+  }
+}
+
 // Per-thread batch of chunk tasks kept in flight before any store.
 constexpr int kBatch = 8;
 
@@ -379,6 +452,15 @@ hipError_t launch_index(const DevLayout& L, const int32_t* tokens, int64_t B, in
   hipLaunchKernelGGL(index_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, L, tokens,
                      B, T, cmap, V, canon_out, hash_out, rows_out, pages_out, signs_out,
                      status);
+  return hipGetLastError();
+}
+
+hipError_t launch_records(const DevLayout& L, const int32_t* tokens, int64_t B, int64_t T,
+                          const int32_t* cmap, int64_t V, void* rec, int32_t* status,
+                          hipStream_t s) {
+  const int64_t blocks = (B * T + kRecTok - 1) / kRecTok;
+  hipLaunchKernelGGL(records_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, L, tokens, B,
+                     T, cmap, V, static_cast<uint4*>(rec), status);
   return hipGetLastError();
 }
 

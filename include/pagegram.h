@@ -233,9 +233,41 @@ PG_API int pg_project_gate(const pg_fuse* fuse, const void* e, int64_t B,
                            int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pg_index_records -- the addressing half of the gathered projection
+ * (PageGram §3.1 rows and the Engram notes' per-head rows; the signs of
+ * §3.1): for every head slot hs = (n - n_min) K + k and token t, a
+ * 16-byte record at rec_out + (hs B T + t) 16 holding the row and the
+ * head's sign bits in the order pg_project_gathered's matrix-core fragments
+ * consume them (a format private to the library). Rows of 64 elements only
+ * (PG_EUNSUPPORTED otherwise); B T at most 2^28 (PG_ERANGE). rec_out is
+ * B T n_ord K 16 bytes of device memory, 16-byte aligned. Tokens outside
+ * [0, V) as for pg_index.
+ */
+PG_API int pg_index_records(const pg_layout* layout, const int32_t* tokens,
+                            int64_t B, int64_t T, const int32_t* canon_map,
+                            int64_t V, void* rec_out, int32_t* dev_status,
+                            hipStream_t stream);
+
+/*
+ * pg_project_gathered -- the scalar-gate projection (PageGram §3.1:
+ * out = x + g W e) with e gathered from the table inside the matrix
+ * kernel by pg_index_records' records, so e never goes to memory. Same
+ * results, bit for bit, as pg_gather followed by pg_project_gate. bf16
+ * tables of 64-element rows with at most 2^25 rows, fuse->dtype bf16 and
+ * the scalar gate (PG_EUNSUPPORTED otherwise). W, resid (nullable) and out
+ * as for pg_project_gate; all pointers 16-byte aligned.
+ */
+PG_API int pg_project_gathered(const pg_layout* layout, const pg_table* table,
+                               const pg_fuse* fuse, const void* rec, int64_t B,
+                               int64_t T, const void* W, const void* resid,
+                               void* out, hipStream_t stream);
+
+/*
  * pg_forward -- the whole path, tokens -> out; equal to pg_index_gather
- * followed by pg_project_gate up to float summation order. workspace at
- * least pg_workspace_size(layout, fuse, B, T) bytes (256-byte aligned).
+ * followed by pg_project_gate up to float summation order (bit for bit
+ * where it runs as pg_index_records followed by pg_project_gathered: bf16
+ * tables of 64-element rows under the scalar gate). workspace at least
+ * pg_workspace_size(layout, fuse, B, T) bytes (256-byte aligned).
  */
 PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
                       const pg_fuse* fuse, const int32_t* tokens, int64_t B,

@@ -228,6 +228,46 @@ def test_project_and_forward_validation():
                         None, None, None, 0, None, None) == pg.PG_OK
 
 
+def test_gathered_projection_validation():
+    L = pg.lib()
+    by = ctypes.byref
+    wl = configs.workload(1)
+    lay = layout_of(wl)
+    R = pg.pg_layout_rows(lay)
+    tab = pg.make_table(pg.PG_BF16, FAKE, R)
+    f = pg.make_fuse(pg.PG_GATE_SCALAR, pg.PG_BF16, 768)
+    assert pg.records_bytes(lay, 8 * 2048) == 16 * 8 * 2048 * 2 * 8
+    # pg_index_records: NULL or misaligned output, rows other than 64 wide,
+    # more than 2^28 tokens, empty input
+    assert L.pg_index_records(by(lay), FAKE, 8, 2048, FAKE, 50304, None, None,
+                              None) == pg.PG_EINVAL
+    assert L.pg_index_records(by(lay), FAKE, 8, 2048, FAKE, 50304, FAKE + 8, None,
+                              None) == pg.PG_EINVAL
+    assert L.pg_index_records(by(lay), FAKE, 1 << 15, 1 << 14, FAKE, 50304, FAKE, None,
+                              None) == pg.PG_ERANGE
+    lay12 = pg.make_layout("pagegram", 8, 12, S=4, pages=[3, 3], pad_id=5)
+    assert L.pg_index_records(by(lay12), FAKE, 1, 4, FAKE, 10, FAKE, None,
+                              None) == pg.PG_EUNSUPPORTED
+    assert L.pg_index_records(by(lay), None, 0, 4, None, 0, None, None, None) == pg.PG_OK
+    # pg_project_gathered: NF4 table, Engram gate, fp32 operands, NULL records
+    nf4 = pg.make_table(pg.PG_NF4, FAKE, R, scales=FAKE)
+    assert L.pg_project_gathered(by(lay), by(nf4), by(f), FAKE, 8, 2048, FAKE, None, FAKE,
+                                 None) == pg.PG_EUNSUPPORTED
+    g = pg.make_fuse(pg.PG_GATE_ENGRAM, pg.PG_BF16, 768, M=4, gamma_h=FAKE,
+                     gamma_k=FAKE, gamma_u=FAKE, conv_w=FAKE)
+    assert L.pg_project_gathered(by(lay), by(tab), by(g), FAKE, 8, 2048, FAKE, FAKE, FAKE,
+                                 None) == pg.PG_EUNSUPPORTED
+    f32 = pg.make_fuse(pg.PG_GATE_SCALAR, pg.PG_F32, 768)
+    assert L.pg_project_gathered(by(lay), by(tab), by(f32), FAKE, 8, 2048, FAKE, None, FAKE,
+                                 None) == pg.PG_EUNSUPPORTED
+    assert L.pg_project_gathered(by(lay), by(tab), by(f), None, 8, 2048, FAKE, None, FAKE,
+                                 None) == pg.PG_EINVAL
+    assert L.pg_project_gathered(by(lay), by(tab), by(f), FAKE, 8, 2048, FAKE, FAKE + 4,
+                                 FAKE, None) == pg.PG_EINVAL
+    assert L.pg_project_gathered(by(lay), by(tab), by(f), None, 0, 2048, None, None, None,
+                                 None) == pg.PG_OK
+
+
 def test_magic_remainder_needs_one_correction():
     # The kernels reduce 64-bit hashes with q = floor(x * floor((2^64-1)/P) /
     # 2^64) and one conditional subtraction. Check that q is the quotient or
