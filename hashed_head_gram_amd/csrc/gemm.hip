@@ -196,13 +196,14 @@ struct PipeCfg {
   static constexpr int kLdsBytes = kRingBytes > kStageTileBytes ? kRingBytes : kStageTileBytes;
 };
 
-// Fused gather (pg_forward with a bf16 table of 64-element rows): the E tile
-// of K stage kt is head slot kt of the tile's tokens, so its rows are table
-// rows, loaded straight into the ring from the table. A token-order's page
-// is hashed once per tile; the first BM lanes hash the heads (and sign
-// words) of stage kt + 3 while stage kt is multiplied. The +-1 signs are
-// applied to the E fragments after the LDS read, with 16-byte XOR masks
-// looked up by sign byte in an LDS table.
+// Gathered projection (pg_forward with a bf16 table of 64-element rows):
+// the E tile of K stage kt is head slot kt of the tile's tokens, so its rows
+// are table rows, loaded straight into the ring from the table by the
+// per-(head slot, token) records records_kernel wrote. The records of a
+// head slot are DMA'd into LDS three stages ahead, the rows of a stage read
+// from them into registers one stage before the stage's DMA, and the +-1
+// signs applied to the E fragments after the LDS read (a shift, an AND and
+// an XOR per dword, the sign bits being pre-arranged in fragment order).
 struct GatherArgs {
   const uint8_t* table;        // [R][64] bf16 rows (R * 128 bytes < 2^32)
   const uint8_t* rec;          // [K / 64][M] records {row, sign words of the two
@@ -321,15 +322,23 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
     dma16(mat + (rb * ld + (int64_t)kt * BK) * EB,
           (uint32_t)(rr * ld * EB) + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)), lds);
   };
+  // fused gather: the lane's table rows of the next stage to load (head
+  // slot hs, token rows grp * RPI + dr), read from the records one stage
+  // before their DMA so the DMA waits on no LDS read
+  uint32_t nrow[GATHER ? A_DMA : 1];
+  auto read_rows = [&](int hs) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int j = 0; j < A_DMA; ++j) nrow[j] = recL[hs % 4][(wave * A_DMA + j) * RPI + dr].x;
+    }
+  };
   auto issue_a = [&](int kt) {
     const uint32_t la = lds0 + (kt % S) * Cfg::kABytes + wave * A_DMA * 1024;
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
       if constexpr (GATHER) {
-        // lane's row: table row of head slot kt of token row grp * RPI + dr
         const int grp = wave * A_DMA + j;
-        const uint32_t row = recL[kt % 4][grp * RPI + dr].x;
-        dma16(ga.table, row * 128u + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)),
+        dma16(ga.table, nrow[j] * 128u + (chunk_b ^ (uint32_t)(swz(grp * RPI) * 16)),
               la + j * 1024);
       } else {
         issue_rows(A, lda, M, m0 + (wave * A_DMA + j) * RPI, wave * A_DMA + j, kt,
@@ -429,10 +438,10 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
   constexpr int NMF = FM * FN;                  // MFMAs per step
   constexpr int RPM = (RD + NMF - 1) / NMF;     // reads issued after each MFMA
   if constexpr (GATHER) {
-    issue_rec(0);
-    if (KT > 1) issue_rec(1);
+    for (int hs = 0; hs < 3 && hs < KT; ++hs) issue_rec(hs);
     wait_vmcnt<0>();
     __syncthreads();
+    read_rows(0);
   }
 #pragma unroll
   for (int st = 0; st < PD; ++st)
@@ -440,6 +449,7 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
       issue_b(st);
       issue_a(st);
     }
+  if (GATHER && KT > 1) read_rows(1);
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt are done when at most the later issued
     // stages (up to PD - 1 of them) are outstanding
@@ -453,20 +463,26 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
     block_sync();
     // the stage that reuses the buffers of stage kt-1 goes out at once, so
     // its load latency overlaps this stage's whole matrix work (fused
-    // gather: after the records of head slot kt + 2, one stage ahead of its
-    // rows; the ring is then one stage deep, so the wait at the top of the
-    // next step covers both)
-    if (GATHER && kt + 2 < KT) issue_rec(kt + 2);
+    // gather: after the records of head slot kt + 3, whose buffer was last
+    // read in step kt - 1; the ring is then one stage deep, so the wait at
+    // the top of the next step covers both; the rows of stage kt + 2 are
+    // then read from their landed records)
+    if (GATHER && kt + 3 < KT) issue_rec(kt + 3);
     if (kt + PD < KT) {
       issue_b(kt + PD);
       issue_a(kt + PD);
     }
+    if (GATHER && kt + 2 < KT) read_rows(kt + 2);
     // fused gather: this lane half's sign words of the stage's E rows
     uint32_t sgn[FM];
     if constexpr (GATHER) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint4 r = recL[kt % 4][wm * WTM + i * 32 + fr];
+        // the whole record in one 16-byte read: consecutive lanes read
+        // consecutive records, free of bank conflicts (two 4-byte reads at
+        // a 16-byte stride are not)
+        uint4 r = recL[kt % 4][wm * WTM + i * 32 + fr];
+        asm volatile("" : "+v"(r.x), "+v"(r.w));
         sgn[i] = lane < 32 ? r.y : r.z;
       }
     }
