@@ -322,8 +322,9 @@ def backward_bench(args):
             "backward_tokens_per_s": N / ((bw_ms + up_ms) / 1e3)}
 
 
-def cpu_baseline(wl, n_tok):
-    """The CPU oracle on the first n_tok tokens of the workload's stream."""
+def cpu_baseline(wl, n_tok, min_seconds=10.0, max_batches=64):
+    """The CPU oracle on successive n_tok-token batches of the workload's
+    stream (distinct seeded batches), until about min_seconds of timed work."""
     import numpy as np
 
     import oracle
@@ -333,34 +334,17 @@ def cpu_baseline(wl, n_tok):
     T = wl["T"]
     B = max(1, min(wl["B"], n_tok // T)) if n_tok >= T else 1
     Tn = T if n_tok >= T else n_tok
-    sub = configs.with_tokens(wl, B, Tn)
-    toks = synth.tokens(wl)[:B, :Tn]
     cmap = synth.canon_map(wl)
     pad = wl["canon_vocab"]
     lay = wl["layout"]
-    # Materialise the touched rows and the dense inputs first (input
-    # generation, not timed).
-    idx = oracle.index(lay, toks, cmap, pad)
-    uniq = np.unique(idx["rows"].reshape(-1))
-    stored = synth.table_rows(wl, uniq)
-
-    def fetch(rows):
-        at = np.searchsorted(uniq, rows)
-        if isinstance(stored, tuple):
-            return stored[0][at], stored[1][at]
-        return stored[at]
     W = synth.weight(wl)
     if wl["act_dtype"] == "bf16":
         W = synth.bf16_bits_to_f32(W)
     N = B * Tn
-    t0 = time.perf_counter()
     if wl["gate"] == "scalar":
         x = synth.resid_rows(wl, np.arange(N))
         if wl["act_dtype"] == "bf16":
             x = synth.bf16_bits_to_f32(x)
-        t0 = time.perf_counter()
-        oracle.forward_scalar(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["g"],
-                              lambda p: x[p])
     else:
         gh, gk, gu, cw = synth.engram_params(wl)
         M, Ntot = wl["M"], wl["B"] * wl["T"]
@@ -368,22 +352,39 @@ def cpu_baseline(wl, n_tok):
                                              + np.arange(Tn)[None, :]).reshape(-1)
                                  for m in range(M)])
         hh = synth.bf16_bits_to_f32(synth.resid_rows(wl, rows_h)).reshape(M, N, -1)
+    total, batches = 0.0, 0
+    while batches < max_batches and (batches == 0 or total < min_seconds):
+        toks = synth.tokens(wl, batch=batches)[:B, :Tn]
+        # Materialise the touched rows first (input generation, not timed).
+        idx = oracle.index(lay, toks, cmap, pad)
+        uniq = np.unique(idx["rows"].reshape(-1))
+        stored = synth.table_rows(wl, uniq)
+
+        def fetch(rows, uniq=uniq, stored=stored):
+            at = np.searchsorted(uniq, rows)
+            if isinstance(stored, tuple):
+                return stored[0][at], stored[1][at]
+            return stored[at]
         t0 = time.perf_counter()
-        oracle.forward_engram(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["d"],
-                              M, gh, gk, gu, cw, wl["conv_dil"], wl["eps"],
-                              lambda m, f: hh[m, f])
-    dt = time.perf_counter() - t0
-    del sub
+        if wl["gate"] == "scalar":
+            oracle.forward_scalar(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["g"],
+                                  lambda p: x[p])
+        else:
+            oracle.forward_engram(lay, pad, toks, cmap, wl["table_dtype"], fetch, W, wl["d"],
+                                  M, gh, gk, gu, cw, wl["conv_dil"], wl["eps"],
+                                  lambda m, f: hh[m, f])
+        total += time.perf_counter() - t0
+        batches += 1
     try:
         from threadpoolctl import threadpool_info
         blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas = 1
-    return {"value": N / dt / 1e6, "unit": "Mtok/s", "cores": int(blas),
+    return {"value": batches * N / total / 1e6, "unit": "Mtok/s", "cores": int(blas),
             "kind": "oracle",
-            "sample": f"first {B}x{Tn} tokens of the stream ({N} tokens), {dt:.2f} s; "
-                      f"index and gather single-threaded numpy, fp64 GEMM on "
-                      f"{blas} BLAS threads"}
+            "sample": f"{batches} batches of {B}x{Tn} tokens ({batches * N} tokens, the "
+                      f"first batches of the seeded stream), {total:.1f} s timed; index and "
+                      f"gather single-threaded numpy, fp64 GEMM on {blas} BLAS threads"}
 
 
 def host_table_bench(args):
