@@ -432,6 +432,33 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
   // is done reading stage kt-1, whose buffers then take stage kt+S-1, issued
   // right there. Within a stage the fragment reads of K step st+1 go out one
   // after each MFMA of step st (LDS latency hides behind issued matrix work).
+  // The epilogue's input tile (the residual x, or h) in registers: chunk q
+  // of this thread is item tid + NT q of the row-major 8-column chunks. The
+  // first PRE_EARLY chunks are requested at the top of the last K stage, so
+  // their latency hides behind its matrix work (as many as the registers
+  // allow beside the fragments); the rest before the epilogue's first pass.
+  constexpr int R = Cfg::kPassRows;
+  constexpr int NP = BM / R;                    // epilogue passes
+  constexpr int ITEMS = R * CPR / NT;           // items per thread per pass
+  static_assert(R * CPR % NT == 0, "epilogue items");
+  constexpr int PRE_EARLY = BN <= 192 ? NP * ITEMS : ITEMS;
+  // A full tile (every row and column inside, N a multiple of 8) takes the
+  // branch-free path; edge tiles check each element.
+  const bool full = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
+  uint4 pre[NP * ITEMS];
+  auto load_pre = [&](int q0, int q1) {
+#pragma unroll
+    for (int q = 0; q < NP * ITEMS; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (pre_ok && full) {
+        const int idx = tid + q * NT;
+        pre[q] = *reinterpret_cast<const uint4*>(pre_src + (m0 + idx / CPR) * pre_ld + pre_c0 +
+                                                 (idx % CPR) * 8);
+      } else {
+        pre[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
   const int KT = K / BK;
   constexpr int PD = S - 1;                     // stages in flight
   constexpr int RD = (FM + FN) * CPF;           // LDS reads per step
@@ -473,6 +500,7 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
       issue_a(kt + PD);
     }
     if (GATHER && kt + 2 < KT) read_rows(kt + 2);
+    if (kt == KT - 1) load_pre(0, PRE_EARLY);
     // fused gather: this lane half's sign words of the stage's E rows
     uint32_t sgn[FM];
     if constexpr (GATHER) {
@@ -540,32 +568,14 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
   // residual tile before the first store (the fragment registers are free
   // by then), so no load is ever waited for behind a store.
   float* tile = reinterpret_cast<float*>(smem);
-  constexpr int R = Cfg::kPassRows;
   constexpr int RS = Cfg::kRowStride;
-  constexpr int NP = BM / R;                    // passes
-  constexpr int ITEMS = R * CPR / NT;     // items per thread per pass
-  static_assert(R * CPR % NT == 0, "epilogue items");
   auto lds_barrier = [] {
     __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // A full tile (every row and column inside, N a multiple of 8) takes the
-  // branch-free path; edge tiles check each element.
-  const bool full = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
-  uint4 pre[NP * ITEMS];
-  if (pre_ok && full) {
-#pragma unroll
-    for (int q = 0; q < NP * ITEMS; ++q) {
-      const int idx = tid + q * NT;
-      pre[q] = *reinterpret_cast<const uint4*>(pre_src + (m0 + idx / CPR) * pre_ld + pre_c0 +
-                                               (idx % CPR) * 8);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < NP * ITEMS; ++q) pre[q] = make_uint4(0, 0, 0, 0);
-  }
+  load_pre(PRE_EARLY, NP * ITEMS);
   // Engram: this thread's 8 columns are the same in every item (CPR divides
   // the thread count), so the gain products are read once.
   float gg[8];
