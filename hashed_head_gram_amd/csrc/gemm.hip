@@ -465,18 +465,22 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
   constexpr int NMF = FM * FN;                  // MFMAs per step
   constexpr int RPM = (RD + NMF - 1) / NMF;     // reads issued after each MFMA
   if constexpr (GATHER) {
+    // the first records, and W's first stage (which waits for none)
     for (int hs = 0; hs < 3 && hs < KT; ++hs) issue_rec(hs);
+    issue_b(0);
     wait_vmcnt<0>();
     __syncthreads();
     read_rows(0);
-  }
+    issue_a(0);
+    if (KT > 1) read_rows(1);
+  } else {
 #pragma unroll
-  for (int st = 0; st < PD; ++st)
-    if (st < KT) {
-      issue_b(st);
-      issue_a(st);
-    }
-  if (GATHER && KT > 1) read_rows(1);
+    for (int st = 0; st < PD; ++st)
+      if (st < KT) {
+        issue_b(st);
+        issue_a(st);
+      }
+  }
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt are done when at most the later issued
     // stages (up to PD - 1 of them) are outstanding

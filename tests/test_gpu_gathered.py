@@ -16,7 +16,7 @@ import hashed_head_gram_amd as pg
 import oracle
 import synth
 from synth import configs
-from tests.gpu_inputs import Case
+from tests.gpu_inputs import Case, rel_err
 from tests.test_gpu_parity import small_wl
 
 pytestmark = pytest.mark.gpu
@@ -111,6 +111,27 @@ def test_records_flag_out_of_range_tokens():
     assert st.item() == 1
     words = rec.view(torch.int32).cpu().numpy().view(np.uint32).reshape(c.O * c.K, c.N, 4)
     assert np.array_equal(words[:, :, 0].T.astype(np.int64), ref["rows"].reshape(c.N, -1))
+
+
+def test_forward_flags_out_of_range_tokens_on_the_gathered_path():
+    wl = small_wl(1, pages=[11, 13], B=2, T=40, d=64)
+    toks = synth.tokens(configs.with_tokens(wl, 2, 40))
+    toks[0, 5] = -1
+    toks[1, 39] = wl["vocab"]
+    c = Case(wl, tokens=toks)
+    f = c.fuse()
+    ws = torch.empty(pg.pg_workspace_size(c.layout, f, c.B, c.T), dtype=torch.uint8,
+                     device=c.dev)
+    st = torch.zeros(1, dtype=torch.int32, device=c.dev)
+    out = c.out_buffer()
+    pg.pg_forward(c.layout, c.table, f, c.tokens, c.cmap, c.W, c.resid, out, ws, dev_status=st)
+    e = c.run_index_gather()
+    want = c.run_project(e)
+    torch.cuda.synchronize()
+    assert st.item() == 1
+    assert torch.equal(out.view(torch.uint8), want.view(torch.uint8))
+    ref = c.oracle_scalar(np.arange(c.N))["out"]
+    assert rel_err(out.double().cpu().numpy(), ref) < 2e-2
 
 
 def test_gathered_rejects_other_tables_and_gates():
