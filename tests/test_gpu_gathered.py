@@ -31,6 +31,11 @@ CASES = {
     "engram_B4_T2_d64": small_wl(2, B=4, T=2, d=64),
     "orders_1to4_K2_B2_T513_d520": small_wl(1, K=2, S=4, n_min=1, n_max=4,
                                             pages=[5, 7, 11, 13], B=2, T=513, d=520),
+    # one and two K stages (E = 64, 128)
+    "one_slot_K1_B2_T300_d192": small_wl(1, K=1, n_min=2, n_max=2, pages=[97], B=2, T=300,
+                                         d=192),
+    "two_slots_K2_B1_T257_d256": small_wl(1, K=2, n_min=3, n_max=3, pages=[53], B=1, T=257,
+                                          d=256),
 }
 
 
