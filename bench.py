@@ -555,6 +555,38 @@ def host_table_bench(args):
     }
 
 
+def records_graph_ms(records_call, rec, steps):
+    """Per-launch GPU time of pg_index_records: `steps` launches (cycling the
+    token pool) captured in one HIP graph, replayed three times; the records
+    after the last replay must equal an eager launch's."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    n = max(1, min(steps, 64))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        records_call(0)
+        with torch.cuda.graph(g, stream=s):
+            for j in range(n):
+                records_call(j)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / n
+        best = t if best is None else min(best, t)
+    got = rec.clone()
+    records_call(n - 1)
+    torch.cuda.synchronize()
+    if not torch.equal(got, rec):
+        raise RuntimeError("graph-replayed records differ from an eager launch's")
+    return best
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -729,6 +761,7 @@ def main():
     g_ms = np.array([per_launch_ms(gather_call)])
     p_ms = np.array([per_launch_ms(project_call)])
     gp_ms = np.array([per_launch_ms(gathered_call)]) if gathered else None
+    rec_ms = records_graph_ms(records_call, rec, args.steps) if gathered else None
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -777,6 +810,9 @@ def main():
             # records_kernel: the rest of a step (K launches of the pair take
             # step_ms_gpu_events each)
             "records_kernel_ms_derived": step_gpu_ms - float(gp_ms.mean()),
+            # records_kernel alone: K launches captured in a HIP graph and
+            # replayed (a launch costs the host more than this kernel takes)
+            "records_kernel_ms": rec_ms,
             "records_bytes_per_launch": N * (4 + 16 * OK)}
         stages["pg_project_gathered_ms"] = float(gp_ms.mean())
         roof = {"kernel": gathered_rec["kernel"], "bound": "mfma", "achieved": gp_tflops,
