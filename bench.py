@@ -1,28 +1,38 @@
 """Throughput of the n-gram memory hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only]
+                    [--no-cpu-baseline] [--no-cold] [--fp8]
 
 A step is one pg_forward call over one batch of synthetic tokens: canonical
-map, n-grams, hashes, rows, gather/dequant/sign, concatenation, W_V
-projection and fusion. Steps cycle through a pool of 32 distinct token
-batches already resident in HBM, so the table rows of one step are not left
-in the caches by the previous one.
+map, n-grams, hashes, rows, gather/dequant/sign, concatenation, projection
+and fusion. Steps cycle through a pool of 32 distinct token batches already
+resident in HBM, so the table rows of one step are not left in the caches by
+the previous one.
 
-The timed region is K steps back to back (wall clock and HIP events around
-it). Each kernel's launch duration is then measured the same way, K launches
-of that stage's entry point alone between HIP events on the stream it runs
-on: pg_index_gather and pg_project_gate, the two calls pg_forward makes
-(checked bit for bit once).
+The headline workload is the largest one that fits one GPU: the Engram-27B
+style fusion layer (32 x 4096 tokens, 5.7B-parameter bf16 table, the fused
+[W_V; W_K^(1..4)] projection of 12,800 x 1,280, context gate and causal
+conv). Its timed region is K steps back to back (wall clock for the value;
+a HIP event before each step for the median, p10 and p90), after a warm-up
+of at least W steps and at least one second. Each kernel's launch durations
+are then measured alone, K launches of its entry point between HIP events on
+the stream it runs on (pg_index_gather, pg_engram_project, pg_engram_gate,
+pg_engram_mix for the Engram workload; pg_forward is checked bit for bit
+against them). A cold variant times single steps after a 1 GiB device write
+that evicts the caches (the write is outside the timed interval).
+
+The other workloads (the 200M PageGram and Engram-style tables and the 20B
+NF4 table) follow as extra keys with the same per-kernel figures, fewer
+steps and no cold variant (--only skips them).
 
 Prints one JSON line: whole-job tokens/s, the roofline position of the
-dominant kernel (algorithmic bytes or flops per launch over its mean launch
-duration), both kernels' figures, and the CPU oracle timed on a bounded
-sample on the host cores.
+dominant kernel (algorithmic flops or bytes per launch over its mean launch
+duration), every kernel's figures, the measured streaming-read rate of the
+GPU, and the CPU oracle timed on a bounded sample on the host cores.
 
---fp8 times the same path with E4M3 projection operands instead
-(pg_forward_fp8 = pg_index_gather_fp8 + pg_project_gate_fp8; W quantised
-once before timing): a separate line at another precision, never the
-headline.
+--fp8 times the same path with E4M3 projection operands instead (W
+quantised once before timing): a separate line at another precision, never
+the headline.
 """
 import argparse
 import hashlib
@@ -39,7 +49,14 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 POOL = 32
-DEFAULT_WORKLOAD = "pagegram200m_bf16_8x2048"
+DEFAULT_WORKLOAD = "engram27b_fusion_bf16_32x4096"
+SECONDARY = ["pagegram200m_bf16_8x2048", "engram200m_bf16_8x2048", "pagegram20b_nf4_16x4096"]
+SECONDARY_STEPS = 200           # timed steps of the extra workloads (at most)
+WARM_S = 1.0                    # seconds of untimed steps before the headline timing
+WARM_S_SECONDARY = 0.3
+COLD_STEPS = 20                 # single steps after a cache-evicting write
+FLUSH_BYTES = 1 << 30
+READ_PROBE_BYTES = 4 << 30
 # E4M3 scale exponents of the --fp8 mode: e ~ N(0, 0.02) rows (NF4: |e| <=
 # about 0.05) and W ~ N(0, 0.05) times 2^s stay well below 448
 FP8_E_SCALE = {"bf16": 11, "nf4": 13, "f32": 11}
@@ -49,13 +66,15 @@ FP8_W_SCALE = 10
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    # about 0.1 s of untimed steps: the GPU reaches its steady clocks before
-    # the timed region (20 steps measure 10-15% slower)
-    p.add_argument("--warmup", type=int, default=2000)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20,
+                   help="untimed steps before timing (and at least one second of them)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--only", action="store_true", help="the headline workload alone")
+    p.add_argument("--no-cold", action="store_true", help="skip the cache-evicted variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=16384)
+    p.add_argument("--cpu-tokens", type=int, default=None,
+                   help="tokens per oracle batch (default: one sequence, at most 16,384)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (for counter scaling)")
     p.add_argument("--backward", action="store_true",
@@ -91,15 +110,23 @@ def algorithmic_costs(wl, fp8=False):
     row_bytes = {"f32": 4 * r, "bf16": 2 * r, "nf4": r // 2 + 2}[wl["table_dtype"]]
     E = O * K * r
     gather_bytes = 4 + O * K * row_bytes + E * e_elt
+    extra = {}
     if wl["gate"] == "engram":
         M, d = wl["M"], wl["d"]
+        n_cb = d // 256
         flops = 2 * E * (1 + M) * d
         proj_bytes = E * e_elt + 2 * M * d * elt   # e in; h in, out (pass 1 + 2 read h)
+        # pass 1: e and h in; v and the partial sums (sum v^2; per branch
+        # sum k^2, sum gamma_h gamma_k h k, sum h^2 per 256 columns) out.
+        # pass 2: h and v in, out out (the gates are 8 M bytes per token).
+        extra = dict(pass1_bytes=E * e_elt + M * d * elt + d * elt + 4 * n_cb * (1 + 3 * M),
+                     pass2_bytes=2 * M * d * elt + d * elt + 8 * M)
     else:
         d = wl["d"]
         flops = 2 * E * d
         proj_bytes = E * e_elt + 2 * d * elt       # e in; x in, out
-    return dict(gather_bytes=gather_bytes, proj_flops=flops, proj_bytes=proj_bytes, E=E)
+    return dict(gather_bytes=gather_bytes, proj_flops=flops, proj_bytes=proj_bytes, E=E,
+                **extra)
 
 
 def source_digest(paths):
@@ -114,6 +141,8 @@ KERNEL_SOURCES = {
     "gather": ["hashed_head_gram_amd/csrc/index.hip", "hashed_head_gram_amd/csrc/common.h"],
     "projection": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
     "gathered": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
+    "pass1": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
+    "pass2": ["hashed_head_gram_amd/csrc/engram.hip", "hashed_head_gram_amd/csrc/common.h"],
 }
 
 
@@ -133,7 +162,8 @@ def traffic_for(stage, workload):
 
 COPY_BYTES = 1 << 30
 TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_kernel",
-                   "gathered": "gemm_pipe_gather_kernel", "copy": "copyBuffer"}
+                   "gathered": "gemm_pipe_gather_kernel", "pass2": "engram_pass2_kernel",
+                   "copy": "copyBuffer"}
 
 
 def counter_means(path, counter):
@@ -166,13 +196,17 @@ def write_traffic(workload, fetch_csv, write_csv):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
-    for stage in ("gather", "projection", "gathered"):
+    from synth import configs
+    engram = configs.workload(workload.split("/")[0])["gate"] == "engram"
+    for stage in ("gather", "projection", "gathered", "pass2"):
         if stage not in fetch or stage not in write:
             continue
         rd = fetch[stage] * 1024 * f_scale
         wr = write[stage] * 1024 * w_scale
-        ent[stage] = {"kernel": TRAFFIC_KERNELS[stage],
-                      "source_digest": source_digest(KERNEL_SOURCES[stage]),
+        # the Engram workload's matrix kernel is pass 1 of the fusion
+        key = "pass1" if engram and stage == "projection" else stage
+        ent[key] = {"kernel": TRAFFIC_KERNELS[stage],
+                      "source_digest": source_digest(KERNEL_SOURCES[key]),
                       "fetch_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
                       "fetch_kib_raw": fetch[stage], "write_kib_raw": write[stage]}
     ent["copy_scale"] = {"fetch": f_scale, "write": w_scale,
@@ -322,16 +356,26 @@ def backward_bench(args):
             "backward_tokens_per_s": N / ((bw_ms + up_ms) / 1e3)}
 
 
-def cpu_baseline(wl, n_tok, min_seconds=10.0, max_batches=64):
-    """The CPU oracle on successive n_tok-token batches of the workload's
-    stream (distinct seeded batches), until about min_seconds of timed work."""
+def cpu_baseline(wl, n_tok=None, min_seconds=10.0, max_batches=64):
+    """The CPU oracle on successive batches of the workload's stream
+    (distinct seeded batches; one sequence each by default, at most 16,384
+    tokens), until about min_seconds of timed work, with BLAS on every core
+    this process may run on."""
     import numpy as np
 
     import oracle
     import synth
-    from synth import configs
 
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(cores)
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = None
     T = wl["T"]
+    if n_tok is None:
+        n_tok = min(16384, max(T, 16384 if wl["gate"] == "scalar" else T))
     B = max(1, min(wl["B"], n_tok // T)) if n_tok >= T else 1
     Tn = T if n_tok >= T else n_tok
     cmap = synth.canon_map(wl)
@@ -375,16 +419,13 @@ def cpu_baseline(wl, n_tok, min_seconds=10.0, max_batches=64):
                                   lambda m, f: hh[m, f])
         total += time.perf_counter() - t0
         batches += 1
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        blas = 1
-    return {"value": batches * N / total / 1e6, "unit": "Mtok/s", "cores": int(blas),
-            "kind": "oracle",
+    return {"value": batches * N / total / 1e6, "unit": "Mtok/s", "cores": cores,
+            "blas_threads": blas, "kind": "oracle",
             "sample": f"{batches} batches of {B}x{Tn} tokens ({batches * N} tokens, the "
-                      f"first batches of the seeded stream), {total:.1f} s timed; index and "
-                      f"gather single-threaded numpy, fp64 GEMM on {blas} BLAS threads"}
+                      f"first batches of the seeded stream), {total:.1f} s timed; index, "
+                      f"gather and the per-token fusion single-threaded numpy, float64 "
+                      f"products on {blas} BLAS threads of the {cores} cores this process "
+                      f"may use"}
 
 
 def host_table_bench(args):
@@ -587,6 +628,374 @@ def records_graph_ms(records_call, rec, steps):
     return best
 
 
+def pct(a, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(a, dtype=np.float64), q))
+
+
+def spread(ms):
+    """mean, median, p10 and p90 of per-launch (or per-step) times in ms."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": pct(a, 50), "p10": pct(a, 10),
+            "p90": pct(a, 90), "n": int(a.size)}
+
+
+def per_launch(fn, n):
+    """Launch durations of fn(j) on the current stream: the mean of n
+    launches back to back between two HIP events, then n more with an event
+    before each and after the last for the median, p10 and p90 (an event
+    between launches adds a few microseconds to short kernels, so the mean
+    comes from the bracket alone)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for j in range(n):
+        fn(j)
+    b.record()
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) / n
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    for j in range(n):
+        ev[j].record()
+        fn(j)
+    ev[n].record()
+    torch.cuda.synchronize()
+    rec = spread([ev[j].elapsed_time(ev[j + 1]) for j in range(n)])
+    rec["mean"] = mean
+    return rec
+
+
+def warm(fn, count, seconds):
+    """At least `count` calls and at least `seconds` of wall clock (the GPU
+    reaches its steady clocks before anything is timed)."""
+    import torch
+    t0 = time.perf_counter()
+    j = 0
+    while j < count or time.perf_counter() - t0 < seconds:
+        fn(j)
+        j += 1
+        if j % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return j
+
+
+class Flush:
+    """Evicts the L2 caches and the 256 MB last-level cache between cold
+    iterations: a 1 GiB device write (torch's fill kernel), outside the
+    timed interval."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(self.k & 0xFF)
+
+
+def cold_steps(forward, n, flush):
+    """n iterations of (flush; event; forward(j); event): per-step ms."""
+    import torch
+    out = []
+    for j in range(n):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        forward(j)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def build(wl, fp8):
+    """Device inputs of one workload (resident in HBM) and the calls that
+    make up its step."""
+    import numpy as np
+    import torch
+
+    import hashed_head_gram_amd as pg
+    import synth
+    from synth import configs, device as sdev
+
+    dev = torch.device("cuda:0")
+    lay_d = wl["layout"]
+    layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
+                            pages=lay_d["pages"], head_rows=lay_d["head_rows"],
+                            hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
+                            n_min=lay_d["n_min"], n_max=lay_d["n_max"],
+                            pad_id=wl["canon_vocab"])
+    R = pg.pg_layout_rows(layout)
+    r = lay_d["r"]
+    B, T = wl["B"], wl["T"]
+    N = B * T
+    costs = algorithmic_costs(wl, fp8)
+    E = costs["E"]
+    if fp8 and (wl["act_dtype"] != "bf16" or E % 128):
+        sys.exit(f"--fp8 needs bf16 activations and an e dimension that is a multiple of "
+                 f"128 ({wl['name']}: {wl['act_dtype']}, {E})")
+    act = torch.float32 if wl["act_dtype"] == "f32" else torch.bfloat16
+    e_dtype = pg.PG_F32 if wl["act_dtype"] == "f32" else pg.PG_BF16
+    keep = {}
+    if wl["table_dtype"] == "nf4":
+        codes = torch.empty(R, r // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(R, dtype=torch.float16, device=dev)
+        sdev.fill_nf4_table(codes, scales, wl["table_seed"])
+        table = pg.make_table(pg.PG_NF4, codes, R, scales=scales)
+    else:
+        tdt = torch.float32 if wl["table_dtype"] == "f32" else torch.bfloat16
+        tab = torch.empty(R, r, dtype=tdt, device=dev)
+        sdev.fill_normal(tab, wl["table_seed"], configs.STREAM_TABLE, wl["table_sigma"])
+        table = pg.make_table(pg.PG_F32 if wl["table_dtype"] == "f32" else pg.PG_BF16,
+                              tab, R)
+    cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
+    pool = [torch.from_numpy(synth.tokens(wl, batch=j)).to(dev) for j in range(POOL)]
+    d_out = configs.d_out(wl)
+    W = torch.empty(d_out, E, dtype=act, device=dev)
+    sdev.fill_normal(W, wl["data_seed"], configs.STREAM_W, wl["w_sigma"])
+    engram = wl["gate"] == "engram"
+    if engram:
+        M = wl["M"]
+        gh, gk, gu, cw = (torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+                          for a in synth.engram_params(wl))
+        fuse = pg.make_fuse(pg.PG_GATE_ENGRAM, e_dtype, wl["d"], M=M, eps=wl["eps"],
+                            gamma_h=gh, gamma_k=gk, gamma_u=gu, conv_w=cw,
+                            conv_k=wl["conv_k"], conv_dil=wl["conv_dil"])
+        resid = torch.empty(M * N, wl["d"], dtype=act, device=dev)
+        out = torch.empty(M * N, wl["d"], dtype=act, device=dev)
+    else:
+        fuse = pg.make_fuse(pg.PG_GATE_SCALAR, e_dtype, wl["d"], g=wl["g"])
+        resid = torch.empty(N, wl["d"], dtype=act, device=dev)
+        out = torch.empty(N, wl["d"], dtype=act, device=dev)
+    sdev.fill_normal(resid, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
+    ws = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8, device=dev)
+    e = torch.empty(N, E, dtype=torch.uint8 if fp8 else act, device=dev)
+    ws2 = torch.empty(max(pg.pg_workspace_size(None, fuse, B, T), 256), dtype=torch.uint8,
+                      device=dev)
+    keep.update(table=table, cmap=cmap, pool=pool, W=W, fuse=fuse, resid=resid, out=out,
+                ws=ws, e=e, ws2=ws2)
+    calls = {}
+    if fp8:
+        se = FP8_E_SCALE[wl["table_dtype"]]
+        sw = FP8_W_SCALE
+        W8 = torch.empty(d_out, E, dtype=torch.uint8, device=dev)
+        pg.pg_quantize_fp8(W, pg.PG_BF16, sw, W8)
+        keep["W8"] = W8
+
+        def forward(j):
+            pg.pg_forward_fp8(layout, table, fuse, pool[j % POOL], cmap, W8, se, sw, resid,
+                              out, ws)
+
+        calls["gather"] = lambda j: pg.pg_index_gather_fp8(layout, table, pool[j % POOL],
+                                                           cmap, se, e)
+        if engram:
+            calls["pass1"] = lambda j: pg.pg_engram_project_fp8(fuse, e, B, T, W8, se, sw,
+                                                                resid, ws2)
+        else:
+            calls["projection"] = lambda j: pg.pg_project_gate_fp8(fuse, e, B, T, W8, se, sw,
+                                                                   resid, out, ws2)
+    else:
+        def forward(j):
+            pg.pg_forward(layout, table, fuse, pool[j % POOL], cmap, W, resid, out, ws)
+
+        calls["gather"] = lambda j: pg.pg_index_gather(layout, table, pool[j % POOL], cmap,
+                                                       e_dtype, e)
+        if engram:
+            calls["pass1"] = lambda j: pg.pg_engram_project(fuse, e, B, T, W, resid, ws2)
+        else:
+            calls["projection"] = lambda j: pg.pg_project_gate(fuse, e, B, T, W, resid, out,
+                                                               ws2)
+    if engram:
+        calls["gate"] = lambda j: pg.pg_engram_gate(fuse, B, T, ws2)
+        calls["pass2"] = lambda j: pg.pg_engram_mix(fuse, B, T, resid, out, ws2)
+    # pg_forward runs as pg_index_records -> pg_project_gathered (E gathered
+    # inside the matrix kernel) for bf16 tables of 64-element rows under the
+    # scalar gate; otherwise as pg_index_gather -> pg_project_gate.
+    gathered = (not fp8 and wl["table_dtype"] == "bf16" and r == 64 and not engram)
+    if gathered:
+        rec = torch.empty(pg.records_bytes(layout, N), dtype=torch.uint8, device=dev)
+        keep["rec"] = rec
+        calls["records"] = lambda j: pg.pg_index_records(layout, pool[j % POOL], cmap, rec)
+        calls["gathered"] = lambda j: pg.pg_project_gathered(layout, table, fuse, rec, B, T,
+                                                             W, resid, out)
+    return dict(wl=wl, N=N, R=R, E=E, costs=costs, fp8=fp8, engram=engram,
+                gathered=gathered, forward=forward, calls=calls, out=out, keep=keep,
+                layout=layout)
+
+
+def check_compositions(b):
+    """pg_forward equals its stage calls bit for bit: the two-kernel path
+    (and the gathered pair where pg_forward takes it)."""
+    import torch
+    out, c = b["out"], b["calls"]
+    b["forward"](0)
+    ref = out.clone()
+
+    def same():
+        torch.cuda.synchronize()
+        return bool(torch.equal(out.view(torch.uint8), ref.view(torch.uint8)))
+    two = ["gather", "pass1", "gate", "pass2"] if b["engram"] else ["gather", "projection"]
+    for k in two:
+        c[k](0)
+    res = {"forward_matches_two_stage": same()}
+    if b["gathered"]:
+        c["records"](0)
+        c["gathered"](0)
+        res["forward_matches_gathered_pair"] = same()
+    del ref
+    return res
+
+
+def run_workload(name, args, primary):
+    """Timed figures of one workload: the whole step and each kernel."""
+    import torch
+
+    from synth import configs
+
+    wl = configs.workload(name)
+    b = build(wl, args.fp8)
+    N, costs, calls = b["N"], b["costs"], b["calls"]
+    eq = check_compositions(b)
+    steps = args.steps if primary else min(args.steps, SECONDARY_STEPS)
+    nwarm = warm(b["forward"], args.warmup, WARM_S if primary else WARM_S_SECONDARY)
+
+    # Timed region: K whole steps (pg_forward) back to back, a HIP event
+    # before each step, synchronised on both sides.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        ev[j].record()
+        b["forward"](j)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_spread = spread([ev[j].elapsed_time(ev[j + 1]) for j in range(steps)])
+    step_spread["mean"] = ev[0].elapsed_time(ev[steps]) / steps
+
+    # Per-kernel launch durations: K launches of each stage call alone.
+    kern = {k: per_launch(fn, steps) for k, fn in calls.items() if k != "records"}
+    if b["gathered"]:
+        kern["records"] = {"mean": records_graph_ms(calls["records"], b["keep"]["rec"], steps)}
+    cold = None
+    if primary and not args.no_cold:
+        flush = Flush(torch.device("cuda:0"))
+        cold = spread(cold_steps(b["forward"], min(steps, COLD_STEPS), flush))
+        del flush
+
+    ms_per_step = wall / steps * 1e3
+    tkey = wl["name"] + ("/fp8" if args.fp8 else "")
+    fp8 = args.fp8
+    p_peak = (FP8_PEAK_TFLOPS if fp8 else
+              FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS)
+    g_bytes = costs["gather_bytes"] * N
+    g = kern["gather"]
+    gather_rec = {"kernel": "index_gather_kernel", "ms": g, "bytes_per_launch": g_bytes,
+                  "achieved_GBps": g_bytes / (g["mean"] / 1e3) / 1e9,
+                  "frac_hbm_peak": g_bytes / (g["mean"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                  "traffic": traffic_for("gather", tkey)}
+    rec = {"workload": wl["name"], "tokens_per_step": N, "value": N / (ms_per_step / 1e3) / 1e6,
+           "ms_per_step": ms_per_step, "step_ms_gpu_events": step_spread,
+           "warmup_steps_run": nwarm, "gather": gather_rec}
+    rec.update(eq)
+    p_flops = costs["proj_flops"] * N
+    if b["engram"]:
+        p1 = kern["pass1"]
+        tf = p_flops / (p1["mean"] / 1e3) / 1e12
+        p1_bytes = costs["pass1_bytes"] * N
+        rec["pass1"] = {"kernel": "gemm_pipe_kernel (Engram pass 1: [W_V; W_K] GEMM + "
+                                  "partial-sum epilogue)", "ms": p1,
+                        "flops_per_launch": p_flops, "achieved_TFLOPs": tf,
+                        "frac_mfma_peak": tf / p_peak, "bytes_per_launch": p1_bytes,
+                        "achieved_GBps": p1_bytes / (p1["mean"] / 1e3) / 1e9,
+                        "traffic": traffic_for("pass1", tkey)}
+        p2 = kern["pass2"]
+        p2_bytes = costs["pass2_bytes"] * N
+        rec["pass2"] = {"kernel": "engram_pass2_kernel", "ms": p2,
+                        "bytes_per_launch": p2_bytes,
+                        "achieved_GBps": p2_bytes / (p2["mean"] / 1e3) / 1e9,
+                        "frac_hbm_peak": p2_bytes / (p2["mean"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                        "traffic": traffic_for("pass2", tkey)}
+        rec["gate"] = {"kernel": "engram_gate_kernel", "ms": kern["gate"]}
+        roof = {"kernel": "gemm_pipe_kernel", "bound": "mfma", "achieved": tf,
+                "peak": p_peak, "unit": "TFLOP/s", "frac": tf / p_peak,
+                "traffic": rec["pass1"]["traffic"]}
+    else:
+        pj = kern["projection"]
+        tf = p_flops / (pj["mean"] / 1e3) / 1e12
+        p_bytes = costs["proj_bytes"] * N
+        rec["projection"] = {
+            "kernel": ("gemm_pipe_kernel" if b["E"] % (128 if fp8 else 64) == 0
+                       else "gemm_bf16_kernel") if wl["act_dtype"] == "bf16"
+            else "gemm_f32_kernel",
+            "ms": pj, "flops_per_launch": p_flops, "achieved_TFLOPs": tf,
+            "frac_mfma_peak": tf / p_peak, "bytes_per_launch": p_bytes,
+            "achieved_GBps": p_bytes / (pj["mean"] / 1e3) / 1e9,
+            "traffic": traffic_for("projection", tkey)}
+        roof = {"kernel": rec["projection"]["kernel"], "bound": "mfma", "achieved": tf,
+                "peak": p_peak, "unit": "TFLOP/s", "frac": tf / p_peak,
+                "traffic": rec["projection"]["traffic"]}
+        if b["gathered"]:
+            gp = kern["gathered"]
+            OK = b["E"] // wl["layout"]["r"]
+            gp_bytes = (costs["proj_bytes"] - b["E"] * 2 + OK * (2 * wl["layout"]["r"] + 16)) * N
+            gtf = p_flops / (gp["mean"] / 1e3) / 1e12
+            rec["gathered_projection"] = {
+                "kernel": "gemm_pipe_gather_kernel", "ms": gp, "flops_per_launch": p_flops,
+                "achieved_TFLOPs": gtf, "frac_mfma_peak": gtf / p_peak,
+                "bytes_per_launch": gp_bytes,
+                "achieved_GBps": gp_bytes / (gp["mean"] / 1e3) / 1e9,
+                "traffic": traffic_for("gathered", tkey),
+                "records_kernel_ms": kern["records"]["mean"],
+                "records_bytes_per_launch": N * (4 + 16 * OK)}
+            roof = {"kernel": "gemm_pipe_gather_kernel", "bound": "mfma", "achieved": gtf,
+                    "peak": p_peak, "unit": "TFLOP/s", "frac": gtf / p_peak,
+                    "traffic": rec["gathered_projection"]["traffic"]}
+        elif g["mean"] > pj["mean"]:
+            roof = {"kernel": "index_gather_kernel", "bound": "hbm",
+                    "achieved": gather_rec["achieved_GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": gather_rec["frac_hbm_peak"],
+                    "traffic": gather_rec["traffic"]}
+    rec["roofline"] = roof
+    if cold is not None:
+        rec["cold_step_ms"] = cold
+        rec["cold_value"] = N / (cold["median"] / 1e3) / 1e6
+    rec["config"] = {"workload": wl["name"], "tokens_per_step": N, "batch": wl["B"],
+                     "seq_len": wl["T"], "layout": wl["layout"]["kind"], "K": wl["layout"]["K"],
+                     "S": wl["layout"]["S"], "r": wl["layout"]["r"],
+                     "table_dtype": wl["table_dtype"], "table_rows": b["R"], "d": wl["d"],
+                     "gate": wl["gate"], "token_pool": POOL}
+    if b["engram"]:
+        rec["config"]["M"] = wl["M"]
+        rec["config"]["d_out"] = (1 + wl["M"]) * wl["d"]
+    del b
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def read_peak():
+    """Streaming-read rate of this GPU (GB/s): the library's read probe over
+    a 4 GiB buffer, median of 20 launches."""
+    import torch
+
+    import hashed_head_gram_amd as pg
+    dev = torch.device("cuda:0")
+    buf = torch.ones(READ_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pg.pg_read_probe(buf, sink)
+    t = per_launch(lambda j: pg.pg_read_probe(buf, sink), 20)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GBps": READ_PROBE_BYTES / (t["median"] / 1e3) / 1e9, "bytes": READ_PROBE_BYTES,
+            "ms": t}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -613,247 +1022,56 @@ def main():
               "(the path shards by sequence with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
-    import hashed_head_gram_amd as pg
-    import synth
-    from synth import configs, device as sdev
+    from synth import configs
 
-    dev = torch.device("cuda:0")
-    wl = configs.workload(args.workload)
-    lay_d = wl["layout"]
-    layout = pg.make_layout(lay_d["kind"], lay_d["K"], lay_d["r"], S=lay_d["S"],
-                            pages=lay_d["pages"], head_rows=lay_d["head_rows"],
-                            hash_seed=lay_d["hash_seed"], use_signs=lay_d["use_signs"],
-                            n_min=lay_d["n_min"], n_max=lay_d["n_max"],
-                            pad_id=wl["canon_vocab"])
-    R = pg.pg_layout_rows(layout)
-    r = lay_d["r"]
-    B, T = wl["B"], wl["T"]
-    N = B * T
-    fp8 = args.fp8
-    costs = algorithmic_costs(wl, fp8)
-    E = costs["E"]
-    if fp8 and (wl["act_dtype"] != "bf16" or E % 128):
-        sys.exit(f"--fp8 needs bf16 activations and an e dimension that is a multiple of "
-                 f"128 ({wl['name']}: {wl['act_dtype']}, {E})")
-    act = torch.float32 if wl["act_dtype"] == "f32" else torch.bfloat16
-    e_dtype = pg.PG_F32 if wl["act_dtype"] == "f32" else pg.PG_BF16
-
-    # Inputs, resident in HBM before timing.
-    if wl["table_dtype"] == "nf4":
-        codes = torch.empty(R, r // 2, dtype=torch.uint8, device=dev)
-        scales = torch.empty(R, dtype=torch.float16, device=dev)
-        sdev.fill_nf4_table(codes, scales, wl["table_seed"])
-        table = pg.make_table(pg.PG_NF4, codes, R, scales=scales)
-    else:
-        tdt = torch.float32 if wl["table_dtype"] == "f32" else torch.bfloat16
-        tab = torch.empty(R, r, dtype=tdt, device=dev)
-        sdev.fill_normal(tab, wl["table_seed"], configs.STREAM_TABLE, wl["table_sigma"])
-        table = pg.make_table(pg.PG_F32 if wl["table_dtype"] == "f32" else pg.PG_BF16,
-                              tab, R)
-    cmap = torch.from_numpy(synth.canon_map(wl)).to(dev)
-    pool = [torch.from_numpy(synth.tokens(wl, batch=j)).to(dev) for j in range(POOL)]
-    d_out = configs.d_out(wl)
-    W = torch.empty(d_out, E, dtype=act, device=dev)
-    sdev.fill_normal(W, wl["data_seed"], configs.STREAM_W, wl["w_sigma"])
-    if wl["gate"] == "engram":
-        M = wl["M"]
-        gh, gk, gu, cw = (torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-                          for a in synth.engram_params(wl))
-        fuse = pg.make_fuse(pg.PG_GATE_ENGRAM, e_dtype, wl["d"], M=M, eps=wl["eps"],
-                            gamma_h=gh, gamma_k=gk, gamma_u=gu, conv_w=cw,
-                            conv_k=wl["conv_k"], conv_dil=wl["conv_dil"])
-        resid = torch.empty(M * N, wl["d"], dtype=act, device=dev)
-        out = torch.empty(M * N, wl["d"], dtype=act, device=dev)
-    else:
-        fuse = pg.make_fuse(pg.PG_GATE_SCALAR, e_dtype, wl["d"], g=wl["g"])
-        resid = torch.empty(N, wl["d"], dtype=act, device=dev)
-        out = torch.empty(N, wl["d"], dtype=act, device=dev)
-    sdev.fill_normal(resid, wl["data_seed"], configs.STREAM_RESID, wl["resid_sigma"])
-    ws = torch.empty(pg.pg_workspace_size(layout, fuse, B, T), dtype=torch.uint8, device=dev)
-    # pg_forward's constituents, for per-kernel timing.
-    e = torch.empty(N, E, dtype=torch.uint8 if fp8 else act, device=dev)
-    ws2 = torch.empty_like(ws)
-    if fp8:
-        # E4M3 scale exponents: |e| 2^se and |W| 2^sw stay well below 448
-        se = FP8_E_SCALE[wl["table_dtype"]]
-        sw = FP8_W_SCALE
-        W8 = torch.empty(d_out, E, dtype=torch.uint8, device=dev)
-        pg.pg_quantize_fp8(W, pg.PG_BF16, sw, W8)
-
-        def forward(j):
-            pg.pg_forward_fp8(layout, table, fuse, pool[j % POOL], cmap, W8, se, sw, resid,
-                              out, ws)
-
-        def gather_call(j):
-            pg.pg_index_gather_fp8(layout, table, pool[j % POOL], cmap, se, e)
-
-        def project_call(j):
-            pg.pg_project_gate_fp8(fuse, e, B, T, W8, se, sw, resid, out, ws2)
-    else:
-        def forward(j):
-            pg.pg_forward(layout, table, fuse, pool[j % POOL], cmap, W, resid, out, ws)
-
-        def gather_call(j):
-            pg.pg_index_gather(layout, table, pool[j % POOL], cmap, e_dtype, e)
-
-        def project_call(j):
-            pg.pg_project_gate(fuse, e, B, T, W, resid, out, ws2)
-    # pg_forward runs as pg_index_records -> pg_project_gathered (E gathered
-    # inside the matrix kernel) for bf16 tables of 64-element rows under the
-    # scalar gate; otherwise as pg_index_gather -> pg_project_gate.
-    gathered = (not fp8 and wl["table_dtype"] == "bf16" and r == 64
-                and wl["gate"] == "scalar")
-    if gathered:
-        rec = torch.empty(pg.records_bytes(layout, N), dtype=torch.uint8, device=dev)
-
-        def records_call(j):
-            pg.pg_index_records(layout, pool[j % POOL], cmap, rec)
-
-        def gathered_call(j):
-            pg.pg_project_gathered(layout, table, fuse, rec, B, T, W, resid, out)
-    torch.cuda.synchronize()
-
-    # The stage calls reproduce pg_forward bit for bit.
-    out_fwd = torch.empty_like(out)
-    forward(0)
-    out_fwd.copy_(out)
-    if gathered:
-        records_call(0)
-        gathered_call(0)
-        torch.cuda.synchronize()
-        same = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
-    gather_call(0)
-    project_call(0)
-    torch.cuda.synchronize()
-    same_two_stage = torch.equal(out.view(torch.uint8), out_fwd.view(torch.uint8))
-    if not gathered:
-        same = same_two_stage
-    del out_fwd
-
-    for j in range(args.warmup):
-        forward(j)
-    # Timed region: K whole steps (pg_forward) back to back.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for j in range(args.steps):
-        forward(j)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
-
-    # Per-kernel launch durations: K launches of each stage back to back
-    # between HIP events on the stream they run on.
-    def per_launch_ms(fn):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for j in range(args.steps):
-            fn(j)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-    g_ms = np.array([per_launch_ms(gather_call)])
-    p_ms = np.array([per_launch_ms(project_call)])
-    gp_ms = np.array([per_launch_ms(gathered_call)]) if gathered else None
-    rec_ms = records_graph_ms(records_call, rec, args.steps) if gathered else None
-
-    if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
+    main_rec = run_workload(args.workload, args, primary=True)
+    others = {}
+    if not args.only:
+        for name in SECONDARY:
+            if name != args.workload:
+                others[name] = run_workload(name, args, primary=False)
+    peak = read_peak() if not args.fp8 else None
+    if copy_probe_needed(args):
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        bb = torch.empty_like(a)
         for _ in range(5):
-            b.copy_(a)
+            bb.copy_(a)
         torch.cuda.synchronize()
-
-    ms_per_step = wall / args.steps * 1e3
-    tok_s = N / (ms_per_step / 1e3)
-    g_bytes = costs["gather_bytes"] * N
-    p_flops = costs["proj_flops"] * N
-    p_bytes = costs["proj_bytes"] * N
-    g_gbps = g_bytes / (g_ms.mean() / 1e3) / 1e9
-    p_peak = (FP8_PEAK_TFLOPS if fp8 else
-              FP32_PEAK_TFLOPS if wl["act_dtype"] == "f32" else BF16_PEAK_TFLOPS)
-    tkey = wl["name"] + ("/fp8" if fp8 else "")
-    p_tflops = p_flops / (p_ms.mean() / 1e3) / 1e12
-    gather_rec = {"kernel": "index_gather_kernel", "ms_mean": float(g_ms.mean()),
-                  "bytes_per_launch": g_bytes, "achieved_GBps": g_gbps,
-                  "frac_hbm_peak": g_gbps / HBM_PEAK_GBPS,
-                  "traffic": traffic_for("gather", tkey)}
-    proj = {"kernel": ("gemm_pipe_kernel" if E % (128 if fp8 else 64) == 0 else "gemm_bf16_kernel")
-            if act == torch.bfloat16 else "gemm_f32_kernel",
-            "ms_mean": float(p_ms.mean()), "flops_per_launch": p_flops,
-            "achieved_TFLOPs": p_tflops, "frac_mfma_peak": p_tflops / p_peak,
-            "bytes_per_launch": p_bytes,
-            "achieved_GBps": p_bytes / (p_ms.mean() / 1e3) / 1e9,
-            "traffic": traffic_for("projection", tkey)}
-    sfx = "_fp8" if fp8 else ""
-    stages = {f"pg_index_gather{sfx}_ms": float(g_ms.mean()),
-              f"pg_project_gate{sfx}_ms": float(p_ms.mean())}
-    gathered_rec = None
-    if gathered:
-        # the matrix kernel reads each token's 2K table rows and records
-        # (16 B per head slot) besides x and out
-        OK = costs["E"] // r
-        gp_bytes = (costs["proj_bytes"] - E * 2 + OK * (2 * r + 16)) * N
-        gp_tflops = p_flops / (gp_ms.mean() / 1e3) / 1e12
-        gathered_rec = {
-            "kernel": "gemm_pipe_gather_kernel", "ms_mean": float(gp_ms.mean()),
-            "flops_per_launch": p_flops, "achieved_TFLOPs": gp_tflops,
-            "frac_mfma_peak": gp_tflops / p_peak, "bytes_per_launch": gp_bytes,
-            "achieved_GBps": gp_bytes / (gp_ms.mean() / 1e3) / 1e9,
-            "traffic": traffic_for("gathered", tkey),
-            # records_kernel: the rest of a step (K launches of the pair take
-            # step_ms_gpu_events each)
-            "records_kernel_ms_derived": step_gpu_ms - float(gp_ms.mean()),
-            # records_kernel alone: K launches captured in a HIP graph and
-            # replayed (a launch costs the host more than this kernel takes)
-            "records_kernel_ms": rec_ms,
-            "records_bytes_per_launch": N * (4 + 16 * OK)}
-        stages["pg_project_gathered_ms"] = float(gp_ms.mean())
-        roof = {"kernel": gathered_rec["kernel"], "bound": "mfma", "achieved": gp_tflops,
-                "peak": p_peak, "unit": "TFLOP/s", "frac": gp_tflops / p_peak,
-                "traffic": gathered_rec["traffic"]}
-    elif g_ms.mean() >= p_ms.mean():
-        roof = {"kernel": gather_rec["kernel"], "bound": "hbm", "achieved": g_gbps,
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": g_gbps / HBM_PEAK_GBPS,
-                "traffic": gather_rec["traffic"]}
-    else:
-        roof = {"kernel": proj["kernel"], "bound": "mfma", "achieved": p_tflops,
-                "peak": p_peak, "unit": "TFLOP/s", "frac": p_tflops / p_peak,
-                "traffic": proj["traffic"]}
+        del a, bb
     cpu = None
-    if not args.no_cpu_baseline and not fp8:
-        cpu = cpu_baseline(wl, args.cpu_tokens)
+    if not args.no_cpu_baseline and not args.fp8:
+        cpu = cpu_baseline(configs.workload(args.workload), args.cpu_tokens)
+    wl = configs.workload(args.workload)
     line = {
         "metric": "M tokens/s for hash+gather+project; gather HBM GB/s and % of peak"
-                  + (" (FP8 E4M3 projection operands)" if fp8 else ""),
-        "value": tok_s / 1e6, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3 operands, fp32 accumulate, bf16 out" if fp8 else wl["act_dtype"],
+                  + (" (FP8 E4M3 projection operands)" if args.fp8 else ""),
+        "value": main_rec["value"], "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_rec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 operands, fp32 accumulate, bf16 out" if args.fp8 else wl["act_dtype"],
         "data": "synthetic (seeded Zipf token streams, counter-generated table and weights)",
-        "config": {"workload": wl["name"], "tokens_per_step": N, "batch": B, "seq_len": T,
-                   "layout": lay_d["kind"], "K": lay_d["K"], "S": lay_d["S"], "r": r,
-                   "table_dtype": wl["table_dtype"], "table_rows": R, "d": wl["d"],
-                   "gate": wl["gate"], "token_pool": POOL},
-        "roofline": roof,
-        "step_ms_gpu_events": step_gpu_ms,
-        "stages": stages,
-        "forward_path": ("pg_index_records -> pg_project_gathered" if gathered else
-                         "pg_index_gather -> pg_project_gate"),
-        "gathered_projection": gathered_rec,
-        "gather": gather_rec,
-        "projection": proj,
-        "forward_matches_stage_calls": bool(same),
-        "forward_matches_two_stage": bool(same_two_stage),
-        "cpu_baseline": cpu,
+        "config": main_rec.pop("config"),
+        "roofline": main_rec.pop("roofline"),
     }
+    if peak is not None:
+        line["measured_read_peak"] = peak
+        g = main_rec["gather"]
+        g["frac_measured_read_peak"] = g["achieved_GBps"] / peak["GBps"]
+        if "pass2" in main_rec:
+            main_rec["pass2"]["frac_measured_read_peak"] = (main_rec["pass2"]["achieved_GBps"]
+                                                            / peak["GBps"])
+    for k in ("value", "ms_per_step"):
+        main_rec.pop(k)
+    line.update(main_rec)
+    line["other_workloads"] = others
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+
+
+def copy_probe_needed(args):
+    return args.copy_probe
 
 
 if __name__ == "__main__":

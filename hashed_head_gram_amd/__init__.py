@@ -73,6 +73,12 @@ _SIGS = {
                                    _vp, _vp, _vp, _i64, _vp]),
     "pg_forward_fp8": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                               _vp, _i64, _vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pg_engram_project": (_i32, [_P(PgFuse), _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "pg_engram_project_fp8": (_i32, [_P(PgFuse), _vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp,
+                                     _vp, _i64, _vp]),
+    "pg_engram_gate": (_i32, [_P(PgFuse), _i64, _i64, _vp, _i64, _vp]),
+    "pg_engram_mix": (_i32, [_P(PgFuse), _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "pg_read_probe": (_i32, [_vp, _i64, _vp, _vp]),
     "pg_strerror": (ctypes.c_char_p, [_i32]),
     "pg_hash_version": (ctypes.c_uint32, []),
     "pg_layout_rows": (_i32, [_P(PgLayout), _P(_i64)]),
@@ -257,6 +263,46 @@ def pg_project_gathered(layout, table, fuse, rec, B, T, W, resid, out, stream=No
     _check("pg_project_gathered", lib().pg_project_gathered(
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(rec), int(B),
         int(T), _ptr(W), _ptr(resid), _ptr(out), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# The Engram gate's three stages (pg_project_gate runs them in order)
+
+
+def _ws_bytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def pg_engram_project(fuse, e, B, T, W, h, workspace, stream=None):
+    _check("pg_engram_project", lib().pg_engram_project(
+        ctypes.byref(fuse), _ptr(e), int(B), int(T), e.shape[-1], _ptr(W), _ptr(h),
+        _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
+
+
+def pg_engram_project_fp8(fuse, e8, B, T, W8, e_scale_exp, w_scale_exp, h, workspace,
+                          stream=None):
+    _check("pg_engram_project_fp8", lib().pg_engram_project_fp8(
+        ctypes.byref(fuse), _ptr(e8), int(B), int(T), e8.shape[-1], _ptr(W8),
+        int(e_scale_exp), int(w_scale_exp), _ptr(h), _ptr(workspace), _ws_bytes(workspace),
+        _stream(stream)))
+
+
+def pg_engram_gate(fuse, B, T, workspace, stream=None):
+    _check("pg_engram_gate", lib().pg_engram_gate(
+        ctypes.byref(fuse), int(B), int(T), _ptr(workspace), _ws_bytes(workspace),
+        _stream(stream)))
+
+
+def pg_engram_mix(fuse, B, T, h, out, workspace, stream=None):
+    _check("pg_engram_mix", lib().pg_engram_mix(
+        ctypes.byref(fuse), int(B), int(T), _ptr(h), _ptr(out), _ptr(workspace),
+        _ws_bytes(workspace), _stream(stream)))
+
+
+def pg_read_probe(src, sink, stream=None):
+    """Streaming read of the whole tensor src (measurement utility)."""
+    _check("pg_read_probe", lib().pg_read_probe(
+        _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagegram.so")
 SOURCES = ["api.hip", "index.hip", "gemm.hip", "engram.hip", "backward.hip", "stage.hip",
-           "pagesim.cpp"]
+           "probe.hip", "pagesim.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

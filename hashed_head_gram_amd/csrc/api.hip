@@ -9,6 +9,7 @@ namespace {
 using pg::DevLayout;
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+constexpr int kReadProbeBlocks = 4096;   // pg_read_probe's grid (one sink word each)
 constexpr int64_t kRowLimit = (int64_t)1 << 62;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -574,6 +575,87 @@ PG_API int pg_forward_fp8(const pg_layout* layout, const pg_table* table, const 
   if (st != PG_OK) return st;
   return run_project_fp8(fuse, e8, B, T, e_dim, W8, e_scale_exp, w_scale_exp, resid, out, ws,
                          stream);
+}
+
+// ---------------------------------------------------------------------------
+// The Engram fusion's three stages (pg_project_gate runs them in order)
+
+namespace {
+
+// Checks shared by the stage calls: an Engram fuse, a workspace of
+// pg_workspace_size(NULL, fuse, B, T) bytes.
+int check_engram_stage(const pg_fuse* f, int64_t B, int64_t T, int64_t e_dim, const void* ws,
+                       int64_t ws_bytes) {
+  const int st = check_fuse(f, B, T, e_dim);
+  if (st != PG_OK) return st;
+  if (f->gate != PG_GATE_ENGRAM) return PG_EINVAL;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!ws || ws_bytes < project_workspace(f, N) || !aligned(ws, 256)) return PG_EINVAL;
+  return PG_OK;
+}
+
+}  // namespace
+
+PG_API int pg_engram_project(const pg_fuse* fuse, const void* e, int64_t B, int64_t T,
+                             int64_t e_dim, const void* W, const void* h, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  const int st = check_engram_stage(fuse, B, T, e_dim, workspace, workspace_bytes);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!e || !W || !h || !aligned(e, 16) || !aligned(W, 16) || !aligned(h, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_engram_project(e, N, e_dim, W, fuse->d, fuse->M, fuse->gamma_h,
+                                              fuse->gamma_k, h, workspace, 0, 0, 0, stream));
+}
+
+PG_API int pg_engram_project_fp8(const pg_fuse* fuse, const uint8_t* e8, int64_t B, int64_t T,
+                                 int64_t e_dim, const uint8_t* W8, int32_t e_scale_exp,
+                                 int32_t w_scale_exp, const void* h, void* workspace,
+                                 int64_t workspace_bytes, hipStream_t stream) {
+  int st = check_fp8_fuse(fuse, B, T, e_dim, e_scale_exp, w_scale_exp);
+  if (st != PG_OK) return st;
+  st = check_engram_stage(fuse, B, T, e_dim, workspace, workspace_bytes);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!e8 || !W8 || !h || !aligned(e8, 16) || !aligned(W8, 16) || !aligned(h, 16))
+    return PG_EINVAL;
+  return hip_status(pg::launch_engram_project(e8, N, e_dim, W8, fuse->d, fuse->M,
+                                              fuse->gamma_h, fuse->gamma_k, h, workspace, 1,
+                                              e_scale_exp, w_scale_exp, stream));
+}
+
+PG_API int pg_engram_gate(const pg_fuse* fuse, int64_t B, int64_t T, void* workspace,
+                          int64_t workspace_bytes, hipStream_t stream) {
+  // e_dim plays no part here; 64 passes the fuse check's e_dim rules
+  const int st = check_engram_stage(fuse, B, T, 64, workspace, workspace_bytes);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  return hip_status(pg::launch_engram_gate(N, fuse->d, fuse->M, fuse->eps, workspace, stream));
+}
+
+PG_API int pg_engram_mix(const pg_fuse* fuse, int64_t B, int64_t T, const void* h, void* out,
+                         void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const int st = check_engram_stage(fuse, B, T, 64, workspace, workspace_bytes);
+  if (st != PG_OK) return st;
+  const int64_t N = B * T;
+  if (N == 0) return PG_OK;
+  if (!h || !out || !aligned(h, 16) || !aligned(out, 16)) return PG_EINVAL;
+  return hip_status(pg::launch_engram_mix(B, T, fuse->d, fuse->M, fuse->gamma_u, fuse->conv_w,
+                                          fuse->conv_k, fuse->conv_dil, h, out, workspace,
+                                          fuse->increment_only ? 0 : 1, stream));
+}
+
+// ---------------------------------------------------------------------------
+// Measurement
+
+PG_API int pg_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16) return PG_EINVAL;
+  if (bytes == 0) return PG_OK;
+  if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4)) return PG_EINVAL;
+  return hip_status(pg::launch_read_probe(src, bytes, sink, kReadProbeBlocks, stream));
 }
 
 // ---------------------------------------------------------------------------

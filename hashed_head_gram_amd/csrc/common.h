@@ -274,11 +274,27 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
                                float* part_v, float* part_k, int f8, int se, int sw,
                                hipStream_t s);
+// The three stages launch_engram runs: pass 1 (v and the partial sums),
+// the per-token gate, pass 2 (conv, SiLU, residual).
+hipError_t launch_engram_project(const void* e, int64_t N, int64_t E, const void* W, int64_t d,
+                                 int64_t M, const float* gamma_h, const float* gamma_k,
+                                 const void* h, void* workspace, int f8, int se, int sw,
+                                 hipStream_t s);
+hipError_t launch_engram_gate(int64_t N, int64_t d, int64_t M, float eps, void* workspace,
+                              hipStream_t s);
+hipError_t launch_engram_mix(int64_t B, int64_t T, int64_t d, int64_t M, const float* gamma_u,
+                             const float* conv_w, int conv_k, int conv_dil, const void* h,
+                             void* out, void* workspace, int add_resid, hipStream_t s);
 hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
                          int64_t d, int64_t M, float eps, const float* gamma_h,
                          const float* gamma_k, const float* gamma_u, const float* conv_w,
                          int conv_k, int conv_dil, const void* h, void* out,
                          void* workspace, int add_resid, int f8, int se, int sw,
                          hipStream_t s);
+
+// Streaming read of bytes (a multiple of 16) at src by `blocks` blocks; one
+// word per block into sink (probe.hip).
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t s);
 
 }  // namespace pg

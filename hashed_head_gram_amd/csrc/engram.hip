@@ -184,38 +184,68 @@ int64_t engram_workspace_bytes(int64_t N, int64_t d, int64_t M) {
          align256(M * 2 * N * 4);
 }
 
-hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
-                         int64_t d, int64_t M, float eps, const float* gamma_h,
-                         const float* gamma_k, const float* gamma_u, const float* conv_w,
-                         int conv_k, int conv_dil, const void* h, void* out,
-                         void* workspace, int add_resid, int f8, int se, int sw,
-                         hipStream_t s) {
-  const int64_t N = B * T;
+namespace {
+
+// The workspace's regions: v [N][d] bf16, sum v^2 partials [n_cb][N], per
+// branch (sum k^2, sum gamma_h gamma_k h k, sum h^2) partials
+// [M][3][n_cb][N], gates [M][2][N] (alpha, RMSNorm_u scale).
+struct EngramWs {
+  uint16_t* v;
+  float* part_v;
+  float* part_k;
+  float* gate;
+};
+
+EngramWs engram_ws(void* workspace, int64_t N, int64_t d, int64_t M) {
   const int64_t n_cb = d / kColBlock;
   auto* base = static_cast<uint8_t*>(workspace);
-  auto* v = reinterpret_cast<uint16_t*>(base);
-  auto* part_v = reinterpret_cast<float*>(base + align256(N * d * 2));
-  auto* part_k = reinterpret_cast<float*>(base + align256(N * d * 2) + align256(n_cb * N * 4));
-  auto* gate = reinterpret_cast<float*>(base + align256(N * d * 2) + align256(n_cb * N * 4) +
-                                        align256(M * 3 * n_cb * N * 4));
-  hipError_t err = launch_engram_pass1(e, N, E, W, d, M, h, gamma_h, gamma_k, v, part_v,
-                                       part_k, f8, se, sw, s);
-  if (err != hipSuccess) return err;
+  EngramWs w;
+  w.v = reinterpret_cast<uint16_t*>(base);
+  base += align256(N * d * 2);
+  w.part_v = reinterpret_cast<float*>(base);
+  base += align256(n_cb * N * 4);
+  w.part_k = reinterpret_cast<float*>(base);
+  base += align256(M * 3 * n_cb * N * 4);
+  w.gate = reinterpret_cast<float*>(base);
+  return w;
+}
+
+}  // namespace
+
+hipError_t launch_engram_project(const void* e, int64_t N, int64_t E, const void* W, int64_t d,
+                                 int64_t M, const float* gamma_h, const float* gamma_k,
+                                 const void* h, void* workspace, int f8, int se, int sw,
+                                 hipStream_t s) {
+  const EngramWs w = engram_ws(workspace, N, d, M);
+  return launch_engram_pass1(e, N, E, W, d, M, h, gamma_h, gamma_k, w.v, w.part_v, w.part_k,
+                             f8, se, sw, s);
+}
+
+hipError_t launch_engram_gate(int64_t N, int64_t d, int64_t M, float eps, void* workspace,
+                              hipStream_t s) {
+  const EngramWs w = engram_ws(workspace, N, d, M);
   hipLaunchKernelGGL(engram_gate_kernel, dim3((unsigned)((N + kThreads - 1) / kThreads),
                                               (unsigned)M),
-                     dim3(kThreads), 0, s, N, (int)d, (int)M, eps, part_v, part_k, (int)n_cb,
-                     gate);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+                     dim3(kThreads), 0, s, N, (int)d, (int)M, eps, w.part_v, w.part_k,
+                     (int)(d / kColBlock), w.gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_engram_mix(int64_t B, int64_t T, int64_t d, int64_t M, const float* gamma_u,
+                             const float* conv_w, int conv_k, int conv_dil, const void* h,
+                             void* out, void* workspace, int add_resid, hipStream_t s) {
+  const int64_t N = B * T;
+  const EngramWs w = engram_ws(workspace, N, d, M);
   dim3 grid((unsigned)((T + kTB - 1) / kTB), (unsigned)B, (unsigned)((d + kCB - 1) / kCB));
   const int rowsL = kTB + (conv_k - 1) * conv_dil;
   const size_t lds = (size_t)rowsL * kCB * 2 + (size_t)2 * M * rowsL * 4;
   const auto* hh = static_cast<const uint16_t*>(h);
   auto* oo = static_cast<uint16_t*>(out);
-#define PG_PASS2(KW)                                                                       \
-  case KW:                                                                                 \
-    hipLaunchKernelGGL(engram_pass2_kernel<KW>, grid, dim3(kThreads), lds, s, T, (int)d,   \
-                       (int)M, gamma_u, conv_w, conv_dil, v, gate, N, hh, oo, add_resid); \
+#define PG_PASS2(KW)                                                                        \
+  case KW:                                                                                  \
+    hipLaunchKernelGGL(engram_pass2_kernel<KW>, grid, dim3(kThreads), lds, s, T, (int)d,    \
+                       (int)M, gamma_u, conv_w, conv_dil, w.v, w.gate, N, hh, oo,           \
+                       add_resid);                                                          \
     break;
   switch (conv_k) {
     PG_PASS2(1) PG_PASS2(2) PG_PASS2(3) PG_PASS2(4) PG_PASS2(5) PG_PASS2(6) PG_PASS2(7)
@@ -225,6 +255,22 @@ hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const v
   }
 #undef PG_PASS2
   return hipGetLastError();
+}
+
+hipError_t launch_engram(const void* e, int64_t B, int64_t T, int64_t E, const void* W,
+                         int64_t d, int64_t M, float eps, const float* gamma_h,
+                         const float* gamma_k, const float* gamma_u, const float* conv_w,
+                         int conv_k, int conv_dil, const void* h, void* out,
+                         void* workspace, int add_resid, int f8, int se, int sw,
+                         hipStream_t s) {
+  const int64_t N = B * T;
+  hipError_t err = launch_engram_project(e, N, E, W, d, M, gamma_h, gamma_k, h, workspace, f8,
+                                         se, sw, s);
+  if (err != hipSuccess) return err;
+  err = launch_engram_gate(N, d, M, eps, workspace, s);
+  if (err != hipSuccess) return err;
+  return launch_engram_mix(B, T, d, M, gamma_u, conv_w, conv_k, conv_dil, h, out, workspace,
+                           add_resid, s);
 }
 
 }  // namespace pg

@@ -277,6 +277,63 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
                       int32_t* dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The Engram gate's three stages (Engram notes §3.3-3.4: the value and key
+ * projections of e, the context gate alpha^m per branch, then the causal
+ * depthwise conv, SiLU and residual; Engram explainer, gate formulas).
+ * pg_project_gate with the Engram gate is exactly pg_engram_project,
+ * pg_engram_gate and pg_engram_mix in that order, on one workspace of
+ * pg_workspace_size(NULL, fuse, B, T) bytes (256-byte aligned) that carries
+ * the intermediate values between them: v = W_V e in bf16 and per-token
+ * partial sums (sum v^2; per branch sum k^2, sum gamma_h gamma_k h k,
+ * sum h^2 over 256-column blocks), then alpha^m and the RMSNorm_u scale.
+ * The workspace's contents between the calls are private to the library.
+ * fuse->gate must be PG_GATE_ENGRAM (PG_EINVAL otherwise) with the limits
+ * of pg_fuse; N = 0 enqueues nothing.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * pg_engram_project -- the fused projection [W_V; W_K^(1..M)] e (pass 1):
+ * v and the partial sums into the workspace; k^m is reduced on chip and
+ * never stored.
+ *   e  [N][e_dim] bf16, W [(1+M) d][e_dim] bf16, h [M][N][d] bf16 (device,
+ *   16-byte aligned).
+ */
+PG_API int pg_engram_project(const pg_fuse* fuse, const void* e, int64_t B,
+                             int64_t T, int64_t e_dim, const void* W,
+                             const void* h, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pg_engram_project_fp8 -- pg_engram_project on E4M3 operands e8 and W8
+ * (scales as for pg_project_gate_fp8; e_dim a multiple of 128).
+ */
+PG_API int pg_engram_project_fp8(const pg_fuse* fuse, const uint8_t* e8,
+                                 int64_t B, int64_t T, int64_t e_dim,
+                                 const uint8_t* W8, int32_t e_scale_exp,
+                                 int32_t w_scale_exp, const void* h,
+                                 void* workspace, int64_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * pg_engram_gate -- per (branch, token): alpha^m = sigmoid(RMSNorm_h(h^m) .
+ * RMSNorm_k(k^m) / sqrt(d)) and alpha^m / sqrt(alpha^m^2 mean(v^2) + eps)
+ * from the partial sums pg_engram_project left in the workspace.
+ */
+PG_API int pg_engram_gate(const pg_fuse* fuse, int64_t B, int64_t T,
+                          void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * pg_engram_mix -- pass 2: out^m = h^m + u^m + SiLU(CausalDWConv(
+ * RMSNorm_u(u^m))) with u^m = alpha^m v (increment_only drops h^m), from
+ * the workspace pg_engram_gate completed.
+ *   h, out [M][N][d] bf16 (device, 16-byte aligned).
+ */
+PG_API int pg_engram_mix(const pg_fuse* fuse, int64_t B, int64_t T,
+                         const void* h, void* out, void* workspace,
+                         int64_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Staging from a host-resident table (PageGram tech report §3.3, Engram
  * notes §3.5: addresses depend only on token IDs and are known before the
  * layer runs, so the touched parts of a table kept in host memory can be
@@ -389,6 +446,17 @@ PG_API int pg_forward_fp8(const pg_layout* layout, const pg_table* table,
                           int32_t w_scale_exp, const void* resid, void* out,
                           void* workspace, int64_t workspace_bytes,
                           int32_t* dev_status, hipStream_t stream);
+
+/*
+ * pg_read_probe -- measurement utility, not part of the path: reads `bytes`
+ * (a multiple of 16) at src once with 16-byte streaming loads, the way the
+ * gather and the Engram pass 2 read HBM, and writes one XOR word per block
+ * into sink (device, 4,096 uint32). Timed by the caller, it gives the read
+ * rate the GPU sustains, the measured ceiling quoted beside the HBM
+ * specification.
+ */
+PG_API int pg_read_probe(const void* src, int64_t bytes, uint32_t* sink,
+                         hipStream_t stream);
 
 /* Message for a pg_status value (static storage). */
 PG_API const char* pg_strerror(int status);

@@ -222,3 +222,75 @@ def test_fp8_entry_points_reject_bad_arguments():
                                0, 0, c.resid, out)
     with pytest.raises(pg.PagegramError):
         pg.pg_quantize_fp8(c.W, pg.PG_NF4, 0, W8)
+
+
+# ---------------------------------------------------------------------------
+# FP8 at the full sizes of the 20B NF4 workload (scalar gate, 65,536 tokens,
+# d = 2560) and of the 27B Engram fusion (131,072 tokens, the fused
+# [W_V; W_K^(1..4)] GEMM of 12,800 x 1,280, gate and conv): sampled
+# positions against the oracle on the dequantised operands.
+
+_full = {}
+
+
+def _full_case(i):
+    if i not in _full:
+        _full.clear()
+        torch.cuda.empty_cache()
+        print(f"[fp8 full] building workload {configs.ORDER[i]}", flush=True)
+        _full[i] = Case(configs.workload(i))
+        torch.cuda.synchronize()
+    return _full[i]
+
+
+def teardown_module(module):
+    _full.clear()
+    torch.cuda.empty_cache()
+
+
+def _sample_positions(c, n_random, seed=0):
+    rng = np.random.default_rng(seed)
+    pos = set()
+    for b in sorted({0, c.B // 2, c.B - 1}):
+        for t in (0, 1, 2, 3, 8, 9, 10, c.T - 2, c.T - 1):
+            pos.add(b * c.T + t)
+    pos |= set(rng.integers(0, c.N, size=n_random).tolist())
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+@pytest.mark.parametrize("i", [3, 4])
+def test_forward_fp8_full_size(i):
+    c = _full_case(i)
+    wl = c.wl
+    se = SE[wl["table_dtype"]]
+    print(f"[fp8 full] {wl['name']} N={c.N} E={c.E} d={c.d}", flush=True)
+    W8, Wq = _w8(c)
+    W8t = _u8(W8, c.dev)
+    f = c.fuse()
+    ws = torch.empty(pg.pg_workspace_size(c.layout, f, c.B, c.T), dtype=torch.uint8,
+                     device=c.dev)
+    out = c.out_buffer()
+    pg.pg_forward_fp8(c.layout, c.table, f, c.tokens, c.cmap, W8t, se, SW, c.resid, out, ws)
+    torch.cuda.synchronize()
+    del ws
+    qt = _Fp8Table(c, se)
+    if wl["gate"] == "scalar":
+        pos = _sample_positions(c, 2000)
+        ref = oracle.forward_scalar(c.lay_d, c.pad, c.tokens_np, c.cmap_np, "bf16", qt.fetch,
+                                    Wq, wl["g"], lambda p: c.resid_rows(p), positions=pos)
+        got = out[torch.from_numpy(pos).to(c.dev)].double().cpu().numpy()
+        tol = TOL
+    else:
+        pos = _sample_positions(c, 24)
+        gh, gk, gu, cw = c.eng_np
+        N = c.N
+        ref = oracle.forward_engram(c.lay_d, c.pad, c.tokens_np, c.cmap_np, "bf16", qt.fetch,
+                                    Wq, c.d, c.M, gh, gk, gu, cw, wl["conv_dil"], wl["eps"],
+                                    lambda m, fl: c.resid_rows([m * N + fl])[0].astype(np.float64),
+                                    positions=pos)
+        sel = torch.from_numpy(pos).to(c.dev)
+        got = np.stack([out[m * N + sel].double().cpu().numpy() for m in range(c.M)])
+        tol = TOL_ENGRAM
+    err = rel_err(got, ref["out"])
+    print(f"[fp8 full] {wl['name']} {len(pos)} positions rel err {err:.3e}", flush=True)
+    assert err < tol

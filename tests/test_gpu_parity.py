@@ -325,3 +325,26 @@ def test_synth_device_fill_matches_host():
     hc, hs = synth.table_rows(wl, np.arange(rows))
     assert_bits_equal(codes.cpu().numpy(), hc, "nf4 codes")
     assert_bits_equal(scales.cpu().numpy().view(np.uint16), hs.view(np.uint16), "nf4 scales")
+
+
+@pytest.mark.parametrize("which", ["ragged", "full"])
+def test_engram_stage_calls_equal_project_gate(which):
+    # pg_project_gate with the Engram gate == pg_engram_project ->
+    # pg_engram_gate -> pg_engram_mix, bit for bit (full and increment-only).
+    c = case(4) if which == "full" else Case(RAGGED["bf16_engram_B2_T45_d256_r24"])
+    e = c.run_index_gather()
+    for inc in (0, 1):
+        out = c.run_project(e, increment_only=inc)
+        f = c.fuse(inc)
+        ws = torch.empty(max(pg.pg_workspace_size(None, f, c.B, c.T), 256), dtype=torch.uint8,
+                         device=c.dev)
+        out2 = c.out_buffer()
+        pg.pg_engram_project(f, e, c.B, c.T, c.W, c.resid, ws)
+        pg.pg_engram_gate(f, c.B, c.T, ws)
+        pg.pg_engram_mix(f, c.B, c.T, c.resid, out2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8)), (which, inc)
+        del ws, out, out2
+    with pytest.raises(pg.PagegramError):        # a scalar-gate fuse is refused
+        fs = pg.make_fuse(pg.PG_GATE_SCALAR, pg.PG_BF16, c.d)
+        pg.pg_engram_gate(fs, c.B, c.T, torch.empty(256, dtype=torch.uint8, device=c.dev))
