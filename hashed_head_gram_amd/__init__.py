@@ -58,6 +58,8 @@ _SIGS = {
                                _vp, _i64, _vp]),
     "pg_forward": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                           _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
+    "pg_forward_noalloc": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
+                                  _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "pg_index_records": (_i32, [_P(PgLayout), _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
     "pg_project_gathered": (_i32, [_P(PgLayout), _P(PgTable), _P(PgFuse), _vp, _i64, _i64,
                                    _vp, _vp, _vp, _vp]),
@@ -245,6 +247,18 @@ def pg_forward(layout, table, fuse, tokens, canon_map, W, resid, out, workspace,
         ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
         B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream)))
+
+
+def pg_forward_noalloc(layout, table, fuse, tokens, canon_map, W, resid, out,
+                       dev_status=None, stream=None):
+    B, T = tokens.shape
+    _check("pg_forward_noalloc", lib().pg_forward_noalloc(
+        ctypes.byref(layout), ctypes.byref(table), ctypes.byref(fuse), _ptr(tokens),
+        B, T, _ptr(canon_map), canon_map.numel(), _ptr(W), _ptr(resid), _ptr(out),
+        _ptr(dev_status), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def records_bytes(layout, n_tok):

@@ -2,6 +2,8 @@
 // Every check that can fail runs before anything is enqueued.
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -307,11 +309,77 @@ PG_API int pg_project_gate(const pg_fuse* fuse, const void* e, int64_t B, int64_
   return run_project(fuse, e, B, T, e_dim, W, resid, out, workspace, stream);
 }
 
+namespace {
+
+// pg_forward's validation and dispatch; `ws == nullptr` with
+// use_scratch set takes the workspace from the device's scratch array.
+int forward_impl(const pg_layout* layout, const pg_table* table, const pg_fuse* fuse,
+                 const int32_t* tokens, int64_t B, int64_t T, const int32_t* canon_map,
+                 int64_t V, const void* W, const void* resid, void* out, void* workspace,
+                 int64_t workspace_bytes, bool use_scratch, int32_t* dev_status,
+                 hipStream_t stream);
+
+}  // namespace
+
 PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_fuse* fuse,
                       const int32_t* tokens, int64_t B, int64_t T, const int32_t* canon_map,
                       int64_t V, const void* W, const void* resid, void* out,
                       void* workspace, int64_t workspace_bytes, int32_t* dev_status,
                       hipStream_t stream) {
+  return forward_impl(layout, table, fuse, tokens, B, T, canon_map, V, W, resid, out,
+                      workspace, workspace_bytes, false, dev_status, stream);
+}
+
+// ---------------------------------------------------------------------------
+// pg_forward_noalloc: pg_forward with its workspace in a file-scope device
+// array, for callers that cannot allocate device memory. Each GPU the
+// library runs on holds one copy of the array (PG_NOALLOC_SCRATCH_BYTES)
+// from the code object's load until the process ends; its device address
+// is looked up once per device and kept. Calls on one GPU share the array,
+// so calls that overlap on one GPU (different streams, different threads)
+// race on it. No kernel of the path relies on the workspace starting at
+// zero (every byte a kernel reads was written earlier in the same call), so
+// nothing is cleared.
+
+static __device__ __align__(256) uint8_t scratch[PG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];   // per device ordinal; null until looked up
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream); the lookup runs once per device, with that
+// device current.
+int scratch_for(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return PG_EHIP;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return PG_EHIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return PG_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PG_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return PG_EHIP;
+    if (e != hipSuccess || !p) return PG_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PG_OK;
+}
+
+int forward_impl(const pg_layout* layout, const pg_table* table, const pg_fuse* fuse,
+                 const int32_t* tokens, int64_t B, int64_t T, const int32_t* canon_map,
+                 int64_t V, const void* W, const void* resid, void* out, void* workspace,
+                 int64_t workspace_bytes, bool use_scratch, int32_t* dev_status,
+                 hipStream_t stream) {
   DevLayout L;
   int st = prepare_layout(layout, &L);
   if (st != PG_OK) return st;
@@ -330,6 +398,12 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
   if (fuse->gate == PG_GATE_ENGRAM && !resid) return PG_EINVAL;
   const int64_t e_bytes = align256(N * e_dim * elt_bytes(fuse->dtype));
   const int64_t need = e_bytes + project_workspace(fuse, N);
+  if (use_scratch) {
+    if (need > PG_NOALLOC_SCRATCH_BYTES) return PG_ERANGE;
+    st = scratch_for(stream, &workspace);
+    if (st != PG_OK) return st;
+    workspace_bytes = PG_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PG_EINVAL;
   // bf16 table rows of 64 elements under the scalar gate: the projection
   // gathers its E operand from the table itself, by per-(head slot, token)
@@ -349,6 +423,17 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table, const pg_f
                                           B, T, canon_map, V, e, dev_status, 0, 0, stream));
   if (st != PG_OK) return st;
   return run_project(fuse, e, B, T, e_dim, W, resid, out, ws, stream);
+}
+
+}  // namespace
+
+PG_API int pg_forward_noalloc(const pg_layout* layout, const pg_table* table,
+                              const pg_fuse* fuse, const int32_t* tokens, int64_t B, int64_t T,
+                              const int32_t* canon_map, int64_t V, const void* W,
+                              const void* resid, void* out, int32_t* dev_status,
+                              hipStream_t stream) {
+  return forward_impl(layout, table, fuse, tokens, B, T, canon_map, V, W, resid, out, nullptr,
+                      0, true, dev_status, stream);
 }
 
 PG_API int pg_index_records(const pg_layout* layout, const int32_t* tokens, int64_t B,

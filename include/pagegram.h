@@ -276,6 +276,30 @@ PG_API int pg_forward(const pg_layout* layout, const pg_table* table,
                       void* workspace, int64_t workspace_bytes,
                       int32_t* dev_status, hipStream_t stream);
 
+/*
+ * pg_forward_noalloc -- pg_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same results, bit for bit, with
+ * the workspace taken from a static device array of PG_NOALLOC_SCRATCH_BYTES
+ * that the library's code object holds on every GPU it runs on until the
+ * process ends. No allocating call is made. The arguments are pg_forward's
+ * without workspace and workspace_bytes. PG_ERANGE when
+ * pg_workspace_size(layout, fuse, B, T) exceeds PG_NOALLOC_SCRATCH_BYTES
+ * (the 200M-parameter workloads' 8 x 2048 tokens fit; the 20B and 27B ones do
+ * not). All calls on one GPU share the array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * The array's device address is looked up on the first call on a GPU (with
+ * that GPU made current for the lookup); PG_EHIP if the lookup fails.
+ */
+#define PG_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+PG_API int pg_forward_noalloc(const pg_layout* layout, const pg_table* table,
+                              const pg_fuse* fuse, const int32_t* tokens,
+                              int64_t B, int64_t T, const int32_t* canon_map,
+                              int64_t V, const void* W, const void* resid,
+                              void* out, int32_t* dev_status,
+                              hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * The Engram gate's three stages (Engram notes §3.3-3.4: the value and key
  * projections of e, the context gate alpha^m per branch, then the causal
