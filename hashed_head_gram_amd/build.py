@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagegram.so")
-SOURCES = ["api.hip", "index.hip", "gemm.hip", "engram.hip", "backward.hip", "stage.hip",
+SOURCES = ["api.hip", "index.hip", "gemm.hip", "gemm_slots.hip", "engram.hip", "backward.hip", "stage.hip",
            "probe.hip", "pagesim.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -38,7 +38,8 @@
 // v = W_V e is stored in bf16 and, per token and 256-column block, the
 // partial sums RMSNorm and the context gate need (sum v^2; per branch sum
 // k^2, sum gamma_h gamma_k h k, sum h^2) go to the workspace, so k is never
-// stored.
+// stored. (Pass 1 on bf16 operands runs on the slot-ring kernel of
+// gemm_slots.hip; this kernel's Engram epilogue serves the E4M3 operands.)
 //
 // Fallback kernel (K a multiple of 8): 128 x 128 tile, BK = 64, register-
 // staged double buffer; scalar gate only.
@@ -1039,7 +1040,8 @@ hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64
 }
 
 // Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller; E %
-// 128 == 0 for FP8 operands, f8 = 1 with scales se, sw).
+// 128 == 0 for FP8 operands, f8 = 1 with scales se, sw). bf16 operands go to
+// the slot-ring kernel, E4M3 operands to the pipelined kernel above.
 hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
                                int64_t d, int64_t Mbr, const void* h,
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
@@ -1060,8 +1062,8 @@ hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* 
     return launch_pipe<256, 256, kPipeBK8, kPipeStages, 1, EPI_ENGRAM, 2, 4, true>(
         e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
   }
-  return launch_pipe<256, 256, kPipeBK, kPipeStages, 1, EPI_ENGRAM, 2, 4>(e, N, (int)((1 + Mbr) * d),
-                                                                   (int)E, W, ep, s);
+  return launch_engram_pass1_slots(e, N, E, W, d, Mbr, h, gamma_h, gamma_k, v, part_v, part_k,
+                                   s);
 }
 
 }  // namespace pg

@@ -1,0 +1,459 @@
+// Pass 1 of the Engram fusion on bf16 operands (gfx950): the fused projection
+// [W_V; W_K^(1..M)] e with its partial-sum epilogue (Engram notes §3.3-3.4:
+// v = W_V e is kept, k^m = W_K^m e only enters RMSNorm(k) and the context
+// gate's dot product with RMSNorm(h), so per token and 256-column block the
+// epilogue leaves sum v^2 and, per branch, sum k^2, sum gamma_h gamma_k h k
+// and sum h^2; v goes out in bf16).
+//
+// Y[M x N] = E[M x K] . W[N x K]^T, 256 x 256 block tiles, 512 threads = 8
+// waves (two per SIMD) in a 2 x 4 grid of 128 x 64 wave tiles made of
+// v_mfma_f32_32x32x16_bf16 blocks (W fragment as the A operand, so a lane's
+// accumulators are runs of four consecutive output columns of one token).
+//
+// K is walked in 32-element slots through a ring of four LDS slot buffers
+// (16 KB of E rows and 16 KB of W rows each), filled by direct global->LDS
+// loads (global_load_lds_dwordx4). The DMA of slot s + 4 goes into slot s's
+// buffer as soon as every wave has read slot s, two instructions per wave and
+// K step, spread over two K steps, so three slots of loads stay in flight and
+// no wave's issue stalls behind a burst of them. Fragments are read one K
+// step ahead; one block barrier per slot, in its middle, marks the next slot
+// as landed and the current slot's buffer as free.
+//
+// Epilogue without an accumulator round trip: as the last four slots' buffers
+// free up, their DMA turns to the h tile of the block's branch (a quarter of
+// the 256 x 256 bf16 tile each), so it is in LDS when the loop ends. Each lane
+// then forms its partial sums straight from its accumulators and the h values
+// of the same elements, one cross-lane add pairs the two half-waves holding a
+// token's columns, and the four column waves meet in a small LDS table. v
+// tiles go out through LDS as 16-byte row stores (the ring is free by then).
+// The h tile's and the v staging's 16-byte chunks sit at chunk ^ (row & 31)
+// so a half-wave's reads of one column block hit distinct banks.
+#include "common.h"
+
+namespace pg {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kColBlock = 256;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Direct global->LDS load (see gemm.hip): 16 bytes per lane from base + off,
+// the wave's 1 KiB to LDS address lds (M0). Not tracked by the compiler's
+// wait counting; the ring orders it with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+struct SlotEpi {
+  int d;                   // columns per segment (d of the model)
+  int n_cb;                // d / 256
+  const uint16_t* h;       // [Mbr][M][d]
+  uint16_t* v;             // [M][d]
+  float* part_v;           // [n_cb][M]
+  float* part_k;           // [Mbr][3][n_cb][M]
+  const float* gamma_h;
+  const float* gamma_k;
+};
+
+__global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __restrict__ E,
+                                                             const uint8_t* __restrict__ W,
+                                                             int64_t M, int N, int K,
+                                                             SlotEpi ep) {
+  constexpr int BM = 256, BN = 256, SK = 32, EB = 2, SKB = SK * EB, NSLOT = 4;
+  constexpr int NT = 512, NW = 8, WGN = 4;
+  constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
+  constexpr int LPR = SKB / 16, RPI = 64 / LPR, ROWS_PER_LINE = 256 / SKB;
+  constexpr int E_DMA = BM / RPI / NW, W_DMA = BN / RPI / NW;   // per wave and slot
+  constexpr int LS = E_DMA + W_DMA;
+  constexpr int kSlotE = BM * SKB, kSlotW = BN * SKB;
+  constexpr int kWOff = NSLOT * kSlotE;
+  constexpr int kRingBytes = NSLOT * (kSlotE + kSlotW);
+  constexpr int kRedOff = kRingBytes;
+  constexpr int kLds = kRingBytes + WGN * BM * 3 * 4;
+  static_assert(E_DMA == 2 && W_DMA == 2, "two DMA instructions per operand and slot");
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave / WGN, wn = wave % WGN;
+  // Blocks are renumbered so that each XCD (blocks are dealt round-robin to
+  // the 8 XCDs) runs a contiguous range of tiles, walked in groups of 8 M
+  // tiles N-major: concurrent tiles share their E and W panels in one L2.
+  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  int64_t bid = blockIdx.x;
+  {
+    const int64_t total = nbm * nbn, per = total / 8;
+    if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int64_t per_group = 8 * nbn, g = bid / per_group, local = bid - g * per_group;
+  const int64_t grows = nbm - g * 8 < 8 ? nbm - g * 8 : 8;
+  const int64_t bn = local / grows, bm = g * 8 + (local - bn * grows);
+  const int64_t m0 = bm * BM;
+  const int n0 = (int)(bn * BN);
+  const int seg = n0 / ep.d;               // 0: v, m >= 1: k of branch m
+  const int cl0 = n0 - seg * ep.d;         // first column within the segment
+  const bool full = m0 + BM <= M;
+  const bool use_h = seg > 0;
+  const uint16_t* hsrc = use_h ? ep.h + (int64_t)(seg - 1) * M * ep.d : ep.h;
+  const bool early_h = use_h && full;
+  const int KS = K / SK;                   // slots (K a multiple of 64: KS even)
+
+  // Chunk c of a slot row r sits at c ^ swz(r): the 16 lanes a 16-byte read
+  // serves together hit 16 distinct 16-byte slots of a 256-byte line.
+  auto swz = [](int r) { return (r / ROWS_PER_LINE) & (LPR - 1); };
+  const int dr = lane / LPR;
+  const uint32_t chunk_b = (uint32_t)(((lane % LPR) ^ swz(dr)) * 16);
+  const uint32_t lds0 = lds_u32(smem);
+  // instruction q of this wave loads rows r_base + q RPI + dr of an operand
+  // (rows past its end repeat its last row, never stored); one SGPR base per
+  // operand and slot, the row offsets are loop-invariant
+  auto dma_offsets = [&](int64_t rows, int64_t r00, uint32_t (&off)[2]) -> int64_t {
+    const int64_t r_base = r00 + (int64_t)wave * 2 * RPI;
+    const int64_t rb = r_base < rows ? r_base : rows - 1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t r = r_base + q * RPI + dr;
+      const int64_t rc = r < rows ? r : rows - 1;
+      off[q] = (uint32_t)((rc - rb) * K * EB) + chunk_b;
+    }
+    return rb;
+  };
+  uint32_t offE[2], offW[2];
+  const int64_t rbE = dma_offsets(M, m0, offE);
+  const int64_t rbW = dma_offsets(N, n0, offW);
+  // h tile row r (0..255): quarter r / 64 lives in the buffer of slot
+  // KS - 4 + r / 64 (E part rows 0-31, W part rows 32-63), 512 bytes a row
+  auto hrow_off = [&](int r) -> uint32_t {
+    const int b = (KS - 4 + (r >> 6)) & 3;
+    const int rr = r & 63;
+    return (uint32_t)(rr < 32 ? b * kSlotE + rr * 512 : kWOff + b * kSlotW + (rr - 32) * 512);
+  };
+  // DMA period p (issued between the barriers of slots p and p + 1; the
+  // prologue is periods -4 .. -1) loads slot p + 4 into slot p's buffer, or,
+  // once the slots are out, quarter p + 4 - KS of the h tile; half 0 is the
+  // E rows (h rows 0-31 of the quarter), half 1 the W rows (h rows 32-63).
+  auto period_count = [&](int p) -> int {
+    const int s = p + 4;
+    return (s < KS || (early_h && s - KS < 4)) ? LS : 0;
+  };
+  auto issue_half = [&](int p, int half) {
+    const int s = p + 4;
+    if (s < KS) {
+      const int b = s & 3;
+      if (half == 0) {
+        const uint8_t* base = E + (rbE * K + (int64_t)s * SK) * EB;
+        const uint32_t l = lds0 + b * kSlotE + wave * E_DMA * 1024;
+        dma16(base, offE[0], l);
+        dma16(base, offE[1], l + 1024);
+      } else {
+        const uint8_t* base = W + (rbW * K + (int64_t)s * SK) * EB;
+        const uint32_t l = lds0 + kWOff + b * kSlotW + wave * W_DMA * 1024;
+        dma16(base, offW[0], l);
+        dma16(base, offW[1], l + 1024);
+      }
+    } else if (early_h && s - KS < 4) {
+      // 32 rows: 4 per wave, 2 per instruction (lanes 0-31 and 32-63)
+      const int rw = (s - KS) * 64 + half * 32 + wave * 4;
+      const int p16 = lane & 31;
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(hsrc + (m0 + rw) * (int64_t)ep.d + cl0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rr = q * 2 + (lane >> 5);
+        dma16(base, (uint32_t)(rr * ep.d * 2 + ((p16 ^ ((rw + rr) & 31)) * 16)),
+              lds0 + hrow_off(rw + q * 2));
+      }
+    }
+  };
+  // this wave's loads of slot s have landed when only those of the periods
+  // after the one that issued it (s - 4), up to p_now - 1, are outstanding
+  auto wait_slot = [&](int s, int p_now) {
+    int later = 0;
+    for (int p = s - 3; p < p_now; ++p) later += period_count(p);
+    if (later >= 3 * LS)
+      wait_vm<3 * LS>();
+    else if (later >= 2 * LS)
+      wait_vm<2 * LS>();
+    else if (later >= LS)
+      wait_vm<LS>();
+    else
+      wait_vm<0>();
+  };
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lgkm0 = [] { __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14)); };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // v_mfma_f32_32x32x16_bf16: lane l holds operand row l % 32 and K elements
+  // 8 (l / 32) .. +7 of the step; D element q of lane l is row 8 (q / 4) +
+  // 4 (l / 32) + q % 4 (an output column), column l % 32 (a token).
+  const int fr = lane & 31;
+  bf16x8_t fa[2][FM], fb[2][FN];
+  auto load_step = [&](int s, int t, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+    const int b = s & 3;
+    const uint8_t* se = smem + b * kSlotE;
+    const uint8_t* sw = smem + kWOff + b * kSlotW;
+    const int c = t * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + fr;
+      af[i] = __builtin_bit_cast(bf16x8_t,
+                                 *reinterpret_cast<const uint4*>(se + r * SKB + ((c ^ swz(r)) * 16)));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 32 + fr;
+      bf[j] = __builtin_bit_cast(bf16x8_t,
+                                 *reinterpret_cast<const uint4*>(sw + r * SKB + ((c ^ swz(r)) * 16)));
+    }
+  };
+  auto mma_step = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bf)[FN], bool reads) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    // the step's fragment reads go out one after each of its first MFMAs
+    if (reads) {
+#pragma unroll
+      for (int x = 0; x < FM + FN; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+    }
+  };
+
+  // prologue: periods -4 .. -1 (slots 0-3); slot 0 landed; its step 0 read
+#pragma unroll
+  for (int p = -4; p < 0; ++p) {
+    issue_half(p, 0);
+    issue_half(p, 1);
+  }
+  wait_slot(0, 0);
+  bar();
+  load_step(0, 0, fa[0], fb[0]);
+
+  // Step (s, 0): reads of (s, 1), MFMAs of (s, 0), the second half of period
+  // s - 1. Barrier B_s: slot s + 1 has landed everywhere and slot s is read.
+  // Step (s, 1): the first half of period s, reads of (s + 1, 0), MFMAs.
+  for (int s = 0; s < KS; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (s > 0) issue_half(s - 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(s, 1, fa[1], fb[1]);
+    mma_step(fa[0], fb[0], true);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < KS) wait_slot(s + 1, s);
+    lgkm0();
+    bar();
+    issue_half(s, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool rd = s + 1 < KS;
+    if (rd) load_step(s + 1, 0, fa[0], fb[0]);
+    mma_step(fa[1], fb[1], rd);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  issue_half(KS - 1, 1);
+
+  // ---- epilogue
+  auto lds_barrier = [] {
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  const int hl = lane >> 5;   // which 4-column half of each 8-column group
+  float* red = reinterpret_cast<float*>(smem + kRedOff);   // [wn][256 rows][3]
+  if (use_h) {
+    // this lane's columns within the segment: cl0 + wn 64 + j 32 + 8 g4 + 4 hl + u
+    float gg[FN][4][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = cl0 + wn * WTN + j * 32 + 8 * g4 + 4 * hl + u;
+          gg[j][g4][u] = ep.gamma_h[c] * ep.gamma_k[c];
+        }
+    wait_vm<0>();
+    bar();   // every wave's h rows have landed; every slot has been read
+    if (!early_h) {
+      // edge tile: h rows straight into the freed ring (zeros past M)
+      for (int idx = tid; idx < BM * 32; idx += NT) {
+        const int r = idx >> 5, c = idx & 31;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (m0 + r < M)
+          val = *reinterpret_cast<const uint4*>(hsrc + (m0 + r) * (int64_t)ep.d + cl0 + c * 8);
+        *reinterpret_cast<uint4*>(smem + hrow_off(r) + ((c ^ (r & 31)) * 16)) = val;
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rl = wm * WTM + i * 32 + (lane & 31);
+      const uint8_t* hrow = smem + hrow_off(rl) + hl * 8;
+      // this row block's accumulators, copied out of the accumulator registers
+      // here and nowhere else
+      f32x16_t av[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        av[j] = acc[i][j];
+        asm volatile("" : "+v"(av[j]));
+      }
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        uint2 hv[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int chunk = wn * 8 + j * 4 + g4;
+          hv[g4] = *reinterpret_cast<const uint2*>(hrow + ((chunk ^ (rl & 31)) * 16));
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float h4[4] = {__uint_as_float(hv[g4].x << 16),
+                               __uint_as_float(hv[g4].x & 0xFFFF0000u),
+                               __uint_as_float(hv[g4].y << 16),
+                               __uint_as_float(hv[g4].y & 0xFFFF0000u)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float y = av[j][4 * g4 + u];
+            s0 += y * y;
+            s1 += gg[j][g4][u] * h4[u] * y;
+            s2 += h4[u] * h4[u];
+          }
+        }
+      }
+      s0 += __shfl_xor(s0, 32, 64);
+      s1 += __shfl_xor(s1, 32, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      if (lane < 32) {
+        float* rp = red + (wn * BM + rl) * 3;
+        rp[0] = s0;
+        rp[1] = s1;
+        rp[2] = s2;
+      }
+    }
+  } else {
+    // v tile: bf16 v through the freed ring (rows of 512 bytes, chunk c at
+    // c ^ (row & 31)), then 16-byte row stores
+    wait_vm<0>();
+    bar();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rl = wm * WTM + i * 32 + (lane & 31);
+      f32x16_t av[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        av[j] = acc[i][j];
+        asm volatile("" : "+v"(av[j]));
+      }
+      float s0 = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float y0 = av[j][4 * g4], y1 = av[j][4 * g4 + 1];
+          const float y2 = av[j][4 * g4 + 2], y3 = av[j][4 * g4 + 3];
+          s0 += y0 * y0 + y1 * y1 + y2 * y2 + y3 * y3;
+          const int chunk = wn * 8 + j * 4 + g4;
+          *reinterpret_cast<uint2*>(smem + rl * 512 + ((chunk ^ (rl & 31)) * 16) + hl * 8) =
+              make_uint2(pack2(y0, y1), pack2(y2, y3));
+        }
+      s0 += __shfl_xor(s0, 32, 64);
+      if (lane < 32) red[(wn * BM + rl) * 3] = s0;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < BM * 32 / NT; ++q) {
+      const int idx = tid + q * NT;
+      const int r = idx >> 5, c = idx & 31;
+      const uint4 val = *reinterpret_cast<const uint4*>(smem + r * 512 + ((c ^ (r & 31)) * 16));
+      if (m0 + r < M)
+        *reinterpret_cast<uint4*>(ep.v + (m0 + r) * (int64_t)ep.d + cl0 + c * 8) = val;
+    }
+  }
+  lds_barrier();
+  if (tid < BM) {
+    const int64_t row = m0 + tid;
+    if (row < M) {
+      float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+#pragma unroll
+      for (int w = 0; w < WGN; ++w) {
+        const float* rp = red + (w * BM + tid) * 3;
+        t0 += rp[0];
+        t1 += rp[1];
+        t2 += rp[2];
+      }
+      const int cb = cl0 / kColBlock;
+      if (!use_h) {
+        ep.part_v[(int64_t)cb * M + row] = t0;
+      } else {
+        float* pk = ep.part_k + (int64_t)(seg - 1) * 3 * ep.n_cb * M;
+        pk[((int64_t)0 * ep.n_cb + cb) * M + row] = t0;
+        pk[((int64_t)1 * ep.n_cb + cb) * M + row] = t1;
+        pk[((int64_t)2 * ep.n_cb + cb) * M + row] = t2;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Pass 1 on bf16 operands: e [N][E], W [(1 + Mbr) d][E] (E a multiple of 64,
+// d of 256; checked by the caller).
+hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const void* W,
+                                     int64_t d, int64_t Mbr, const void* h,
+                                     const float* gamma_h, const float* gamma_k, uint16_t* v,
+                                     float* part_v, float* part_k, hipStream_t s) {
+  SlotEpi ep{};
+  ep.d = (int)d;
+  ep.n_cb = (int)(d / kColBlock);
+  ep.h = static_cast<const uint16_t*>(h);
+  ep.v = v;
+  ep.part_v = part_v;
+  ep.part_k = part_k;
+  ep.gamma_h = gamma_h;
+  ep.gamma_k = gamma_k;
+  const int64_t Nout = (1 + Mbr) * d;
+  const int64_t blocks = ((N + 255) / 256) * ((Nout + 255) / 256);
+  hipLaunchKernelGGL(engram_slot_kernel, dim3((unsigned)blocks), dim3(512), 0, s,
+                     static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
+                     (int)Nout, (int)E, ep);
+  return hipGetLastError();
+}
+
+}  // namespace pg
