@@ -141,7 +141,7 @@ KERNEL_SOURCES = {
     "gather": ["hashed_head_gram_amd/csrc/index.hip", "hashed_head_gram_amd/csrc/common.h"],
     "projection": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
     "gathered": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
-    "pass1": ["hashed_head_gram_amd/csrc/gemm.hip", "hashed_head_gram_amd/csrc/common.h"],
+    "pass1": ["hashed_head_gram_amd/csrc/gemm_slots.hip", "hashed_head_gram_amd/csrc/common.h"],
     "pass2": ["hashed_head_gram_amd/csrc/engram.hip", "hashed_head_gram_amd/csrc/common.h"],
 }
 
@@ -162,7 +162,8 @@ def traffic_for(stage, workload):
 
 COPY_BYTES = 1 << 30
 TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_kernel",
-                   "gathered": "gemm_pipe_gather_kernel", "pass2": "engram_pass2_kernel",
+                   "gathered": "gemm_pipe_gather_kernel", "pass1": "engram_slot_kernel",
+                   "pass2": "engram_pass2_kernel",
                    "copy": "copyBuffer"}
 
 
@@ -196,15 +197,12 @@ def write_traffic(workload, fetch_csv, write_csv):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
-    from synth import configs
-    engram = configs.workload(workload.split("/")[0])["gate"] == "engram"
-    for stage in ("gather", "projection", "gathered", "pass2"):
+    for stage in ("gather", "projection", "gathered", "pass1", "pass2"):
         if stage not in fetch or stage not in write:
             continue
         rd = fetch[stage] * 1024 * f_scale
         wr = write[stage] * 1024 * w_scale
-        # the Engram workload's matrix kernel is pass 1 of the fusion
-        key = "pass1" if engram and stage == "projection" else stage
+        key = stage
         ent[key] = {"kernel": TRAFFIC_KERNELS[stage],
                       "source_digest": source_digest(KERNEL_SOURCES[key]),
                       "fetch_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
@@ -907,7 +905,8 @@ def run_workload(name, args, primary):
         p1 = kern["pass1"]
         tf = p_flops / (p1["mean"] / 1e3) / 1e12
         p1_bytes = costs["pass1_bytes"] * N
-        rec["pass1"] = {"kernel": "gemm_pipe_kernel (Engram pass 1: [W_V; W_K] GEMM + "
+        p1_kernel = "gemm_pipe_kernel" if fp8 else "engram_slot_kernel"
+        rec["pass1"] = {"kernel": p1_kernel + " (Engram pass 1: [W_V; W_K] GEMM + "
                                   "partial-sum epilogue)", "ms": p1,
                         "flops_per_launch": p_flops, "achieved_TFLOPs": tf,
                         "frac_mfma_peak": tf / p_peak, "bytes_per_launch": p1_bytes,
@@ -921,7 +920,7 @@ def run_workload(name, args, primary):
                         "frac_hbm_peak": p2_bytes / (p2["mean"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
                         "traffic": traffic_for("pass2", tkey)}
         rec["gate"] = {"kernel": "engram_gate_kernel", "ms": kern["gate"]}
-        roof = {"kernel": "gemm_pipe_kernel", "bound": "mfma", "achieved": tf,
+        roof = {"kernel": p1_kernel, "bound": "mfma", "achieved": tf,
                 "peak": p_peak, "unit": "TFLOP/s", "frac": tf / p_peak,
                 "traffic": rec["pass1"]["traffic"]}
     else:

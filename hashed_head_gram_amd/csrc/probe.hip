@@ -1,8 +1,10 @@
 // Streaming-read probe (gfx950): the HBM read rate this GPU sustains, the
 // measured ceiling the gather and the Engram pass 2 are compared with beside
-// the 8 TB/s specification. Every lane reads 16-byte chunks, four in flight,
-// over a grid-stride walk; the XOR of what it read goes to one word per block
-// so no load can be dropped.
+// the 8 TB/s specification. Each block reads one contiguous chunk of the
+// buffer, every lane eight 16-byte loads in flight per round (contiguous
+// chunks per block stream from HBM faster than a grid-stride walk, which
+// spreads each round over the whole buffer); the XOR of what a block read
+// goes to one word per block so no load can be dropped.
 #include "common.h"
 
 namespace pg {
@@ -10,23 +12,22 @@ namespace pg {
 namespace {
 
 constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;
 
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(
-    const uint4* __restrict__ src, int64_t n16, uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+    const uint4* __restrict__ src, int64_t n16, int64_t chunk, uint32_t* __restrict__ sink) {
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c1 = c0 + chunk < n16 ? c0 + chunk : n16;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i];
-    const uint4 b = src[i + stride];
-    const uint4 c = src[i + 2 * stride];
-    const uint4 d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-           d.z ^ d.w;
-  }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += (int64_t)kProbeThreads * kProbeUnroll) {
+    uint4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const int64_t j = i + (int64_t)u * kProbeThreads;
+      v[u] = j < c1 ? src[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   __shared__ uint32_t red[kProbeThreads / 64];
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
@@ -43,8 +44,10 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(
 
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                              hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  const int64_t chunk = (n16 + blocks - 1) / blocks;
   hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s,
-                     static_cast<const uint4*>(src), bytes / 16, sink);
+                     static_cast<const uint4*>(src), n16, chunk, sink);
   return hipGetLastError();
 }
 

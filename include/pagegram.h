@@ -473,10 +473,11 @@ PG_API int pg_forward_fp8(const pg_layout* layout, const pg_table* table,
 
 /*
  * pg_read_probe -- measurement utility, not part of the path: reads `bytes`
- * (a multiple of 16) at src once with 16-byte streaming loads, the way the
- * gather and the Engram pass 2 read HBM, and writes one XOR word per block
- * into sink (device, 4,096 uint32). Timed by the caller, it gives the read
- * rate the GPU sustains, the measured ceiling quoted beside the HBM
+ * (a multiple of 16) at src once with 16-byte streaming loads, 4,096 blocks
+ * each reading one contiguous chunk, and writes the XOR of the 32-bit words
+ * each block read into sink (device, 4,096 uint32; the XOR of all sink words
+ * is the XOR of all words of the buffer). Timed by the caller, it gives the
+ * read rate the GPU sustains, the measured ceiling quoted beside the HBM
  * specification.
  */
 PG_API int pg_read_probe(const void* src, int64_t bytes, uint32_t* sink,
