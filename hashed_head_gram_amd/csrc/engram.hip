@@ -29,6 +29,8 @@ constexpr int kMaxBranches = 8;  // largest M (validated by the caller)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kTPT = kTB / (kThreads / 32);   // tokens per thread in pass 2
 
 // Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32); a low.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void engram_gate_kernel(
 
 // Dynamic LDS: v window [(TB + H) x 256] bf16, then alpha and the RMSNorm_u
 // scale [M][TB + H] fp32.
-template <int KW>
+template <int KW, int MAXB>
 __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
     int64_t T, int d, int Mbr, const float* __restrict__ gamma_u,
     const float* __restrict__ conv_w, int dil, const uint16_t* __restrict__ v,
@@ -123,6 +125,23 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
   const int cg = tid & 31;
   const int c = c0 + cg * 8;
   if (c >= d) return;
+  // Every h row this thread needs (its kTPT tokens, all branches) is requested
+  // before any arithmetic or store, so a wave keeps MAXB * kTPT 16-byte loads
+  // in flight (stores share the load counter on this GPU, so a load issued
+  // after a store would also wait for it). h and out are streamed once:
+  // non-temporal loads and stores.
+  u32x4 hr[MAXB][kTPT];
+#pragma unroll
+  for (int m = 0; m < MAXB; ++m)
+#pragma unroll
+    for (int k = 0; k < kTPT; ++k) {
+      const int64_t t = t0 + (tid >> 5) + k * (kThreads / 32);
+      if (m < Mbr && t < T && add_resid)
+        hr[m][k] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(h + (((int64_t)m * N + b * T + t) * d + c)));
+      else
+        hr[m][k] = u32x4{0u, 0u, 0u, 0u};
+    }
   // conv weights with the RMSNorm_u gain folded in: wg = w * gamma_u
   float wg[8][kw];
 #pragma unroll
@@ -131,7 +150,9 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
 #pragma unroll
     for (int j = 0; j < kw; ++j) wg[x][j] = conv_w[(c + x) * kw + j] * gu;
   }
-  for (int tl = tid >> 5; tl < kTB; tl += kThreads / 32) {
+#pragma unroll
+  for (int k = 0; k < kTPT; ++k) {
+    const int tl = (tid >> 5) + k * (kThreads / 32);
     const int64_t t = t0 + tl;
     if (t >= T) break;
     const int li = tl + H;  // LDS index of t
@@ -144,12 +165,8 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
       unpack8(*reinterpret_cast<const uint4*>(&vt[(li - (kw - 1 - j) * dil) * kCB + cg * 8]),
               vj[j]);
 #pragma unroll
-    for (int m = 0; m < kMaxBranches; ++m) {
+    for (int m = 0; m < MAXB; ++m) {
       if (m >= Mbr) break;
-      // the residual load goes out before the conv arithmetic
-      const uint4 hr = add_resid ? *reinterpret_cast<const uint4*>(
-                                       h + (((int64_t)m * N + b * T + t) * d + c))
-                                 : make_uint4(0, 0, 0, 0);
       float conv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < kw; ++j) {
@@ -159,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
       }
       const float alpha = alphaS[m * rowsL + li];
       float hv[8];
-      unpack8(hr, hv);
-      uint32_t res[4];
+      unpack8(make_uint4(hr[m][k][0], hr[m][k][1], hr[m][k][2], hr[m][k][3]), hv);
+      u32x4 res;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         // SiLU(y) = y / (1 + e^-y)
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void engram_pass2_kernel(
                              hv[2 * x + 1] + (alpha * vc[2 * x + 1] + y1));
       }
       const int64_t o = ((int64_t)m * N + b * T + t) * d + c;
-      *reinterpret_cast<uint4*>(out + o) = make_uint4(res[0], res[1], res[2], res[3]);
+      __builtin_nontemporal_store(res, reinterpret_cast<u32x4*>(out + o));
     }
   }
 }
@@ -243,9 +260,14 @@ hipError_t launch_engram_mix(int64_t B, int64_t T, int64_t d, int64_t M, const f
   auto* oo = static_cast<uint16_t*>(out);
 #define PG_PASS2(KW)                                                                        \
   case KW:                                                                                  \
-    hipLaunchKernelGGL(engram_pass2_kernel<KW>, grid, dim3(kThreads), lds, s, T, (int)d,    \
-                       (int)M, gamma_u, conv_w, conv_dil, w.v, w.gate, N, hh, oo,           \
-                       add_resid);                                                          \
+    if (M <= 4)                                                                             \
+      hipLaunchKernelGGL((engram_pass2_kernel<KW, 4>), grid, dim3(kThreads), lds, s, T,     \
+                         (int)d, (int)M, gamma_u, conv_w, conv_dil, w.v, w.gate, N, hh, oo, \
+                         add_resid);                                                        \
+    else                                                                                    \
+      hipLaunchKernelGGL((engram_pass2_kernel<KW, kMaxBranches>), grid, dim3(kThreads), lds, \
+                         s, T, (int)d, (int)M, gamma_u, conv_w, conv_dil, w.v, w.gate, N,   \
+                         hh, oo, add_resid);                                                \
     break;
   switch (conv_k) {
     PG_PASS2(1) PG_PASS2(2) PG_PASS2(3) PG_PASS2(4) PG_PASS2(5) PG_PASS2(6) PG_PASS2(7)
