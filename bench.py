@@ -92,9 +92,11 @@ def parse():
                    help="--host-table unit of transfer: pages / 4 KiB runs, or single rows")
     p.add_argument("--fp8", action="store_true",
                    help="E4M3 projection operands (pg_forward_fp8); a separate line")
-    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                   help="write profiles/traffic.json from two rocprofv3 --pmc counter "
-                        "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run")
+    p.add_argument("--traffic-from", nargs="+", metavar="CSV",
+                   help="write profiles/traffic.json from rocprofv3 --pmc counter "
+                        "collections of --copy-probe runs: FETCH_SIZE, WRITE_SIZE and "
+                        "optionally TCC_EA0_RDREQ{,_32B,_64B,_128B}_sum (read requests "
+                        "by size)")
     return p.parse_args()
 
 
@@ -161,6 +163,7 @@ def traffic_for(stage, workload):
 
 
 COPY_BYTES = 1 << 30
+COPY_REPS = 5
 TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_kernel",
                    "gathered": "gemm_pipe_gather_kernel", "pass1": "engram_slot_kernel",
                    "pass2": "engram_pass2_kernel",
@@ -168,30 +171,49 @@ TRAFFIC_KERNELS = {"gather": "index_gather_kernel", "projection": "gemm_pipe_ker
 
 
 def counter_means(path, counter):
-    """Mean per-dispatch value (KiB) of one counter for each kernel family."""
+    """Mean per-dispatch value of one counter for each kernel family (KiB for
+    FETCH_SIZE and WRITE_SIZE, requests for the TCC_EA0_RDREQ family)."""
     import csv
     sums = {}
     for row in csv.DictReader(open(path)):
-        if row["Counter_Name"] != counter:
+        if row["Counter_Name"] not in (counter, counter + "_sum"):
             continue
         for fam, key in TRAFFIC_KERNELS.items():
             if key in row["Kernel_Name"]:
                 d = sums.setdefault(fam, {})
                 d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    # the copy family: only the 1 GiB probe copies (bench.py's other copies are
-    # at most a third of that; FETCH_SIZE reads half of a copy's bytes)
+    # the copy family: only the 1 GiB probe copies, the last COPY_REPS copies
+    # of the run (set-up copies of other sizes, some larger, come before them)
     if "copy" in sums:
-        sums["copy"] = {k: v for k, v in sums["copy"].items() if v * 1024 > 0.45 * COPY_BYTES}
+        last = sorted(sums["copy"], key=int)[-COPY_REPS:]
+        sums["copy"] = {k: sums["copy"][k] for k in last}
     return {fam: sum(d.values()) / len(d) for fam, d in sums.items() if d}
 
 
-def write_traffic(workload, fetch_csv, write_csv):
+def read_bytes_by_size(rdreq_csv):
+    """Bytes read from HBM per dispatch and family from the memory-side read
+    requests counted by size (32, 64 and 128 bytes; requests of none of the
+    three sizes, if any, taken as 64 bytes)."""
+    n = {sz: counter_means(rdreq_csv, "TCC_EA0_RDREQ" + sz) for sz in ("", "_32B", "_64B", "_128B")}
+    out = {}
+    for fam, tot in n[""].items():
+        r32, r64, r128 = (n[sz].get(fam, 0.0) for sz in ("_32B", "_64B", "_128B"))
+        other = max(tot - r32 - r64 - r128, 0.0)
+        out[fam] = {"bytes": 32 * r32 + 64 * (r64 + other) + 128 * r128, "req": tot,
+                    "req_32B": r32, "req_64B": r64, "req_128B": r128}
+    return out
+
+
+def write_traffic(workload, fetch_csv, write_csv, rdreq_csv=None):
     """HBM bytes per launch of the gather and projection kernels (and of the
     gathered projection where the workload runs it): FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
-    1 GiB device copy read and write exactly 1 GiB."""
+    1 GiB device copy read and write exactly 1 GiB. With rdreq_csv, read bytes
+    also from the read requests by size, unscaled, next to the copy's reading
+    of the same counters (which should be 1 GiB)."""
     fetch = counter_means(fetch_csv, "FETCH_SIZE")
     write = counter_means(write_csv, "WRITE_SIZE")
+    by_size = read_bytes_by_size(rdreq_csv) if rdreq_csv else {}
     f_scale = COPY_BYTES / (fetch["copy"] * 1024)
     w_scale = COPY_BYTES / (write["copy"] * 1024)
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -207,8 +229,12 @@ def write_traffic(workload, fetch_csv, write_csv):
                       "source_digest": source_digest(KERNEL_SOURCES[key]),
                       "fetch_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
                       "fetch_kib_raw": fetch[stage], "write_kib_raw": write[stage]}
+        if stage in by_size:
+            ent[key]["read_requests"] = by_size[stage]
     ent["copy_scale"] = {"fetch": f_scale, "write": w_scale,
                          "copy_fetch_kib_raw": fetch["copy"], "copy_write_kib_raw": write["copy"]}
+    if "copy" in by_size:
+        ent["copy_scale"]["copy_read_requests"] = by_size["copy"]
     rec[workload] = ent
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -998,6 +1024,8 @@ def read_peak():
 def main():
     args = parse()
     if args.traffic_from:
+        if len(args.traffic_from) not in (2, 3):
+            sys.exit("--traffic-from takes FETCH_CSV WRITE_CSV [RDREQ_CSV]")
         write_traffic(args.workload, *args.traffic_from)
         return
     if args.backward:
@@ -1035,7 +1063,7 @@ def main():
     if copy_probe_needed(args):
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
         bb = torch.empty_like(a)
-        for _ in range(5):
+        for _ in range(COPY_REPS):
             bb.copy_(a)
         torch.cuda.synchronize()
         del a, bb

@@ -13,7 +13,9 @@
  * Conventions for every entry point
  *   - Pointers named as device pointers are device memory owned by the
  *     caller, contiguous and row-major. The library allocates nothing and
- *     keeps no pointer after it returns. There is no global mutable state.
+ *     keeps no pointer after it returns. The only global state is
+ *     pg_forward_noalloc's static device array and its per-GPU address,
+ *     looked up once under a lock.
  *   - Work is enqueued on `stream` and the call returns without waiting;
  *     results are visible to later work on that stream.
  *   - Return value: PG_OK or a negative pg_status. Errors that the host can
@@ -80,7 +82,9 @@ typedef enum pg_gate {
  *     row_{n,k} = base_{n,k} + (u_{n,k}(x) mod P_{n,k}).
  * The flat table of PageGram §2.1 is PG_PAGEGRAM with K=1, S=1.
  *
- * Hashes (hash version 1; the pages fix only "multiply-XOR"): for an n-gram
+ * Hashes (hash version 1; the Engram notes, section 3.2, fix only a light
+ * multiply-XOR hash per head, and the PageGram tech report, section 3.1, a
+ * page hash b_n beside the head hashes u_{n,k}): for an n-gram
  * g_j = canonical ID at position t-j (j = 0..n-1; pad_id before the start of
  * the sequence) and a role (page hash b_n, head hash u_{n,k}, sign word w of
  * head (n,k)):
@@ -215,7 +219,11 @@ PG_API int pg_index_gather(const pg_layout* layout, const pg_table* table,
                            hipStream_t stream);
 
 /*
- * pg_project_gate -- projection through W and the fusion stage.
+ * pg_project_gate -- projection through W and the fusion stage: the
+ * scalar-gated residual of the PageGram tech report (section 3.1: the memory
+ * vector is projected by W_V and added to the residual stream through a
+ * learned scalar gate), or the Engram notes' context gate, convolution and
+ * branch integration (sections 3.3-3.4), as defined under pg_fuse above.
  *   e        [N][e_dim]              (device, fuse->dtype)
  *   W        [d_out][e_dim]          (device, fuse->dtype), d_out = d, or
  *                                    (1+M)*d for the Engram gate
@@ -263,7 +271,11 @@ PG_API int pg_project_gathered(const pg_layout* layout, const pg_table* table,
                                void* out, hipStream_t stream);
 
 /*
- * pg_forward -- the whole path, tokens -> out; equal to pg_index_gather
+ * pg_forward -- the whole path, tokens -> out: the lookup pipeline of the
+ * Engram explainer (canonical IDs, suffix n-grams, several hashes, table
+ * rows, concatenated e_t), addressed as in the PageGram tech report section
+ * 3.1 or the Engram notes section 3.2, then the fusion of pg_project_gate.
+ * Equal to pg_index_gather
  * followed by pg_project_gate up to float summation order (bit for bit
  * where it runs as pg_index_records followed by pg_project_gathered: bf16
  * tables of 64-element rows under the scalar gate). workspace at least
@@ -486,7 +498,14 @@ PG_API int pg_read_probe(const void* src, int64_t bytes, uint32_t* sink,
 /* Message for a pg_status value (static storage). */
 PG_API const char* pg_strerror(int status);
 
-/* Hash definition version implemented (1, as described above). */
+/*
+ * Hash definition version implemented (1, as described under pg_layout).
+ * The pages fix the hash only as a light multiply-XOR per head (Engram
+ * notes section 3.2; the PageGram tech report section 3.1 adds a separate
+ * page hash b_n next to the head hashes u_{n,k}); the constants and the
+ * splitmix64 finaliser are this library's choice, so the version names the
+ * bit-level definition a stored table was trained with.
+ */
 PG_API uint32_t pg_hash_version(void);
 
 /* Total row count R of a layout; PG_EINVAL / PG_ERANGE for a bad layout. */
