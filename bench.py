@@ -50,6 +50,8 @@ FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 POOL = 32
 DEFAULT_WORKLOAD = "engram27b_fusion_bf16_32x4096"
+BACKWARD_WORKLOAD = "pagegram200m_bf16_8x2048"   # the backward needs the scalar gate
+HOST_TABLE_WORKLOAD = "pagegram200m_bf16_8x2048"  # so does the host-table step
 SECONDARY = ["pagegram200m_bf16_8x2048", "engram200m_bf16_8x2048", "pagegram20b_nf4_16x4096"]
 SECONDARY_STEPS = 200           # timed steps of the extra workloads (at most)
 WARM_S = 1.0                    # seconds of untimed steps before the headline timing
@@ -69,7 +71,9 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20,
                    help="untimed steps before timing (and at least one second of them)")
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--workload", default=None,
+                   help=f"workload name (default {DEFAULT_WORKLOAD}; {BACKWARD_WORKLOAD} "
+                        f"with --backward, {HOST_TABLE_WORKLOAD} with --host-table)")
     p.add_argument("--only", action="store_true", help="the headline workload alone")
     p.add_argument("--no-cold", action="store_true", help="skip the cache-evicted variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,7 +101,11 @@ def parse():
                         "collections of --copy-probe runs: FETCH_SIZE, WRITE_SIZE and "
                         "optionally TCC_EA0_RDREQ{,_32B,_64B,_128B}_sum (read requests "
                         "by size)")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.workload is None:
+        a.workload = (BACKWARD_WORKLOAD if a.backward else
+                      HOST_TABLE_WORKLOAD if a.host_table else DEFAULT_WORKLOAD)
+    return a
 
 
 def algorithmic_costs(wl, fp8=False):

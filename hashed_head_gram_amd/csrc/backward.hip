@@ -25,6 +25,33 @@ constexpr int kDigits = 1 << kRadixBits;
 constexpr int kItems = 8;                          // items per thread
 constexpr int kTile = kThreads * kItems;           // items per block
 
+// Exclusive scan of one int32 per thread across the block (integer sums, so
+// any summation order gives the same values): a shuffle scan inside each
+// wave, then the wave totals. *total gets the block sum. sh holds
+// kThreads / 64 ints; every thread of the block must call it.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t x, int32_t* sh,
+                                                        int32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < kThreads / 64; ++j) {
+    const int32_t t = sh[j];
+    base += j < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();   // sh may be reused by the caller after this
+  *total = tot;
+  return base + v - x;
+}
+
 // ---------------------------------------------------------------------------
 // Transpose (bf16): out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad.
 
@@ -46,6 +73,40 @@ __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
     const int cc = ty + 4 * q;
     const int64_t c = c0 + cc, r = r0 + tx;
     if (c < cols && r < rows_pad) out[c * ld_out + r] = t[tx][cc];
+  }
+}
+
+// The same with 16-byte accesses: a 64 x 64 tile read as rows of eight
+// 16-byte chunks, written as columns of eight. cols, ld_in, rows_pad and
+// ld_out multiples of 8 and both pointers 16-byte aligned (checked by the
+// launcher).
+__global__ __launch_bounds__(kThreads) void transpose_bf16_v8_kernel(
+    const uint16_t* __restrict__ in, int64_t rows, int64_t cols, int64_t ld_in,
+    uint16_t* __restrict__ out, int64_t rows_pad, int64_t ld_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = threadIdx.x + q * kThreads;
+    const int rr = idx >> 3, cc = (idx & 7) * 8;
+    const int64_t r = r0 + rr, c = c0 + cc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(in + r * ld_in + c);
+    *reinterpret_cast<uint4*>(&t[rr][cc]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = threadIdx.x + q * kThreads;
+    const int cc = idx >> 3, rr = (idx & 7) * 8;
+    const int64_t c = c0 + cc, r = r0 + rr;
+    if (c < cols && r < rows_pad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)t[rr + 2 * j][cc] | ((uint32_t)t[rr + 2 * j + 1][cc] << 16);
+      *reinterpret_cast<uint4*>(out + c * ld_out + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -97,25 +158,14 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(
 // In-place exclusive scan of m int32 values by one block; total -> *total.
 __global__ __launch_bounds__(kThreads) void scan_small_kernel(int32_t* __restrict__ a, int64_t m,
                                                              int32_t* __restrict__ total) {
-  __shared__ int32_t sums[kThreads];
+  __shared__ int32_t sh[kThreads / 64];
   const int64_t per = (m + kThreads - 1) / kThreads;
   const int64_t lo = threadIdx.x * per, hi = lo + per < m ? lo + per : m;
   int32_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += a[i];
-  sums[threadIdx.x] = s;
-  __syncthreads();
-  // exclusive scan of the 256 thread sums (thread 0 walks them: 256 adds)
-  if (threadIdx.x == 0) {
-    int32_t run = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int32_t v = sums[t];
-      sums[t] = run;
-      run += v;
-    }
-    if (total) *total = run;
-  }
-  __syncthreads();
-  int32_t run = sums[threadIdx.x];
+  int32_t tot;
+  int32_t run = block_exclusive_scan(s, sh, &tot);
+  if (total && threadIdx.x == 0) *total = tot;
   for (int64_t i = lo; i < hi; ++i) {
     const int32_t v = a[i];
     a[i] = run;
@@ -128,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     const uint32_t* __restrict__ kin, const int32_t* __restrict__ vin, int64_t n, int shift,
     const int32_t* __restrict__ offs, uint32_t* __restrict__ kout, int32_t* __restrict__ vout) {
   __shared__ int32_t F[kDigits * kThreads];       // [digit][thread] counts, then prefixes
-  __shared__ int32_t tsum[kThreads];
+  __shared__ int32_t sh[kThreads / 64];
   const int t = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)t * kItems;
   uint32_t k[kItems];
@@ -159,19 +209,10 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     loc[q] = run;
     run += F[t * kDigits + q];
   }
-  tsum[t] = run;
-  __syncthreads();
-  if (t == 0) {
-    int32_t acc = 0;
-    for (int j = 0; j < kThreads; ++j) {
-      const int32_t x = tsum[j];
-      tsum[j] = acc;
-      acc += x;
-    }
-  }
-  __syncthreads();
+  int32_t tot;
+  const int32_t before = block_exclusive_scan(run, sh, &tot);
 #pragma unroll
-  for (int q = 0; q < kDigits; ++q) F[t * kDigits + q] = loc[q] + tsum[t];
+  for (int q = 0; q < kDigits; ++q) F[t * kDigits + q] = loc[q] + before;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
@@ -194,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
 __global__ __launch_bounds__(kThreads) void seg_flags_kernel(
     const uint32_t* __restrict__ keys, int64_t n, int32_t* __restrict__ flags,
     int32_t* __restrict__ bsum) {
-  __shared__ int32_t s[kThreads];
+  __shared__ int32_t s[kThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
   int32_t c = 0;
 #pragma unroll
@@ -206,13 +247,9 @@ __global__ __launch_bounds__(kThreads) void seg_flags_kernel(
       c += f;
     }
   }
-  s[threadIdx.x] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int j = 0; j < kThreads; ++j) acc += s[j];
-    bsum[blockIdx.x] = acc;
-  }
+  int32_t tot;
+  block_exclusive_scan(c, s, &tot);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
 // Segment id of every head; seg_start[id] = its position; the last block
@@ -221,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void seg_starts_kernel(
     const int32_t* __restrict__ flags, int64_t n, const int32_t* __restrict__ boff,
     const int32_t* __restrict__ total, int32_t* __restrict__ seg_start,
     int64_t* __restrict__ n_unique) {
-  __shared__ int32_t s[kThreads];
+  __shared__ int32_t s[kThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
   int32_t c = 0;
 #pragma unroll
@@ -229,18 +266,8 @@ __global__ __launch_bounds__(kThreads) void seg_starts_kernel(
     const int64_t i = base + q;
     if (i < n) c += flags[i];
   }
-  s[threadIdx.x] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int j = 0; j < kThreads; ++j) {
-      const int32_t x = s[j];
-      s[j] = acc;
-      acc += x;
-    }
-  }
-  __syncthreads();
-  int32_t id = boff[blockIdx.x] + s[threadIdx.x];
+  int32_t tot;
+  int32_t id = boff[blockIdx.x] + block_exclusive_scan(c, s, &tot);
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int64_t i = base + q;
@@ -474,6 +501,21 @@ __global__ void set_i64_kernel(int64_t* p, int64_t v) { *p = v; }
 
 int64_t al(int64_t x) { return (x + 255) / 256 * 256; }
 
+// out[c][r] = in[r][c] (zeros for rows <= r < rows_pad), 16-byte accesses
+// where the shapes and pointers allow.
+void transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld_in,
+                    uint16_t* out, int64_t rows_pad, int64_t ld_out, hipStream_t s) {
+  const dim3 grid((unsigned)((rows_pad + 63) / 64), (unsigned)((cols + 63) / 64));
+  const bool v8 = cols % 8 == 0 && ld_in % 8 == 0 && rows_pad % 8 == 0 && ld_out % 8 == 0 &&
+                  ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0;
+  if (v8)
+    hipLaunchKernelGGL(transpose_bf16_v8_kernel, grid, dim3(kThreads), 0, s, in, rows, cols,
+                       ld_in, out, rows_pad, ld_out);
+  else
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(kThreads), 0, s, in, rows, cols, ld_in,
+                       out, rows_pad, ld_out);
+}
+
 unsigned grid_for(int64_t n, int64_t per_block) {
   int64_t b = (n + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -541,15 +583,12 @@ hipError_t launch_backward_scalar(const DevLayout& Ly, const BackwardPlan& p, fl
   const auto* Wb = static_cast<const uint16_t*>(W);
 
   // de = g dy W: A = dy [N][d], B = W^T [E][d]
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((E + 63) / 64)),
-                     dim3(kThreads), 0, s, Wb, d, E, E, WT, d, d);
+  transpose_bf16(Wb, d, E, E, WT, d, d, s);
   hipError_t err = launch_gemm_f32(dy, (int)d, WT, (int)d, N, (int)E, (int)d, 1, g, de, E, s);
   if (err != hipSuccess) return err;
   // dW = g dy^T e: A = dy^T [d][kpad], B = e^T [E][kpad], split K
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(p.kpad / 64), (unsigned)((d + 63) / 64)),
-                     dim3(kThreads), 0, s, dyb, N, d, d, dyT, p.kpad, p.kpad);
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(p.kpad / 64), (unsigned)((E + 63) / 64)),
-                     dim3(kThreads), 0, s, eb, N, E, E, eT, p.kpad, p.kpad);
+  transpose_bf16(dyb, N, d, d, dyT, p.kpad, p.kpad, s);
+  transpose_bf16(eb, N, E, E, eT, p.kpad, p.kpad, s);
   err = launch_gemm_f32(dyT, (int)p.kpad, eT, (int)p.kpad, d, (int)E, p.kc, p.splits, g, part, E, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid_for(d * E, kThreads)), dim3(kThreads), 0, s,
