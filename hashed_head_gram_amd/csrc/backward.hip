@@ -15,6 +15,7 @@
 //   step: 16 lanes per distinct row apply the replayed decay of the steps
 //   the row missed and the RMS step of this one.
 #include "common.h"
+#include "scan.h"
 
 namespace pg {
 namespace {
@@ -25,32 +26,6 @@ constexpr int kDigits = 1 << kRadixBits;
 constexpr int kItems = 8;                          // items per thread
 constexpr int kTile = kThreads * kItems;           // items per block
 
-// Exclusive scan of one int32 per thread across the block (integer sums, so
-// any summation order gives the same values): a shuffle scan inside each
-// wave, then the wave totals. *total gets the block sum. sh holds
-// kThreads / 64 ints; every thread of the block must call it.
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t x, int32_t* sh,
-                                                        int32_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int32_t v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) sh[w] = v;
-  __syncthreads();
-  int32_t base = 0, tot = 0;
-#pragma unroll
-  for (int j = 0; j < kThreads / 64; ++j) {
-    const int32_t t = sh[j];
-    base += j < w ? t : 0;
-    tot += t;
-  }
-  __syncthreads();   // sh may be reused by the caller after this
-  *total = tot;
-  return base + v - x;
-}
 
 // ---------------------------------------------------------------------------
 // Transpose (bf16): out[c][r] = in[r][c] for r < rows, 0 for rows <= r < rows_pad.
@@ -164,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void scan_small_kernel(int32_t* __restric
   int32_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += a[i];
   int32_t tot;
-  int32_t run = block_exclusive_scan(s, sh, &tot);
+  int32_t run = block_exclusive_scan<kThreads>(s, sh, &tot);
   if (total && threadIdx.x == 0) *total = tot;
   for (int64_t i = lo; i < hi; ++i) {
     const int32_t v = a[i];
@@ -210,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(
     run += F[t * kDigits + q];
   }
   int32_t tot;
-  const int32_t before = block_exclusive_scan(run, sh, &tot);
+  const int32_t before = block_exclusive_scan<kThreads>(run, sh, &tot);
 #pragma unroll
   for (int q = 0; q < kDigits; ++q) F[t * kDigits + q] = loc[q] + before;
   __syncthreads();
@@ -248,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void seg_flags_kernel(
     }
   }
   int32_t tot;
-  block_exclusive_scan(c, s, &tot);
+  block_exclusive_scan<kThreads>(c, s, &tot);
   if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
@@ -267,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void seg_starts_kernel(
     if (i < n) c += flags[i];
   }
   int32_t tot;
-  int32_t id = boff[blockIdx.x] + block_exclusive_scan(c, s, &tot);
+  int32_t id = boff[blockIdx.x] + block_exclusive_scan<kThreads>(c, s, &tot);
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int64_t i = base + q;

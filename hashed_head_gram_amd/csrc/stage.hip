@@ -20,6 +20,7 @@
 //   remap    cache row of each lookup = slot * U + (row - first row)
 // Rows are clamped into the table, so a bad row cannot read outside it.
 #include "common.h"
+#include "scan.h"
 
 namespace pg {
 namespace {
@@ -85,43 +86,29 @@ __global__ __launch_bounds__(kThreads) void stage_insert_kernel(
 __global__ __launch_bounds__(kThreads) void stage_count_kernel(const uint64_t* __restrict__ keys,
                                                                int64_t H,
                                                                int32_t* __restrict__ bcount) {
-  __shared__ int32_t s[kThreads];
+  __shared__ int32_t s[kThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kThreads * kItems + (int64_t)threadIdx.x * kItems;
   int32_t c = 0;
 #pragma unroll
   for (int q = 0; q < kItems; ++q)
     if (base + q < H && keys[base + q] != kEmpty) ++c;
-  s[threadIdx.x] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int j = 0; j < kThreads; ++j) acc += s[j];
-    bcount[blockIdx.x] = acc;
-  }
+  int32_t tot;
+  block_exclusive_scan<kThreads>(c, s, &tot);
+  if (threadIdx.x == 0) bcount[blockIdx.x] = tot;
 }
 
 // Exclusive scan of nb block counts by one block; the total -> *n_units.
 __global__ __launch_bounds__(kThreads) void stage_scan_kernel(int32_t* __restrict__ a,
                                                               int64_t nb,
                                                               int64_t* __restrict__ n_units) {
-  __shared__ int32_t sums[kThreads];
+  __shared__ int32_t sh[kThreads / 64];
   const int64_t per = (nb + kThreads - 1) / kThreads;
   const int64_t lo = threadIdx.x * per, hi = lo + per < nb ? lo + per : nb;
   int32_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += a[i];
-  sums[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t run = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int32_t v = sums[t];
-      sums[t] = run;
-      run += v;
-    }
-    *n_units = run;
-  }
-  __syncthreads();
-  int32_t run = sums[threadIdx.x];
+  int32_t tot;
+  int32_t run = block_exclusive_scan<kThreads>(s, sh, &tot);
+  if (threadIdx.x == 0) *n_units = tot;
   for (int64_t i = lo; i < hi; ++i) {
     const int32_t v = a[i];
     a[i] = run;
@@ -134,24 +121,14 @@ __global__ __launch_bounds__(kThreads) void stage_rank_kernel(
     DevLayout L, int U, const uint64_t* __restrict__ keys, int64_t H,
     const int32_t* __restrict__ boff, int32_t* __restrict__ ranks,
     int64_t* __restrict__ ufirst, int32_t* __restrict__ ucount) {
-  __shared__ int32_t s[kThreads];
+  __shared__ int32_t s[kThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kThreads * kItems + (int64_t)threadIdx.x * kItems;
   int32_t c = 0;
 #pragma unroll
   for (int q = 0; q < kItems; ++q)
     if (base + q < H && keys[base + q] != kEmpty) ++c;
-  s[threadIdx.x] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int j = 0; j < kThreads; ++j) {
-      const int32_t v = s[j];
-      s[j] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  int32_t slot = boff[blockIdx.x] + s[threadIdx.x];
+  int32_t tot;
+  int32_t slot = boff[blockIdx.x] + block_exclusive_scan<kThreads>(c, s, &tot);
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int64_t h = base + q;
