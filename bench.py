@@ -939,7 +939,7 @@ def run_workload(name, args, primary):
         p1 = kern["pass1"]
         tf = p_flops / (p1["mean"] / 1e3) / 1e12
         p1_bytes = costs["pass1_bytes"] * N
-        p1_kernel = "gemm_pipe_kernel" if fp8 else "engram_slot_kernel"
+        p1_kernel = "engram_slot_kernel"
         rec["pass1"] = {"kernel": p1_kernel + " (Engram pass 1: [W_V; W_K] GEMM + "
                                   "partial-sum epilogue)", "ms": p1,
                         "flops_per_launch": p_flops, "achieved_TFLOPs": tf,

@@ -221,12 +221,15 @@ hipError_t launch_project_scalar_fp8(const void* e8, int64_t N, int64_t E, const
                                      int se, int sw, hipStream_t s);
 
 // fp32-output GEMM with optional split K (partials at out + s * M * ldo).
-// Engram pass 1 on bf16 operands through the slot-ring kernel (gemm_slots.hip);
-// E a multiple of 64, d of 256 (checked by the caller).
+// Engram pass 1 through the slot-ring kernel (gemm_slots.hip): bf16
+// operands (E a multiple of 64) or, with f8, E4M3 ones with scales 2^se
+// (e) and 2^sw (W) (E a multiple of 128); d a multiple of 256 (checked by
+// the caller).
 hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const void* W,
                                      int64_t d, int64_t Mbr, const void* h,
                                      const float* gamma_h, const float* gamma_k, uint16_t* v,
-                                     float* part_v, float* part_k, hipStream_t s);
+                                     float* part_v, float* part_k, int f8, int se, int sw,
+                                     hipStream_t s);
 hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64_t M, int N,
                            int Kc, int splits, float g, float* out, int64_t ldo,
                            hipStream_t s);

@@ -8,8 +8,9 @@
 // one wave's matrix work covers the other's barrier and LDS waits; block
 // tile BM x BN (256 x 192 in a 4 x 2 wave grid, or 256 x 256 in 2 x 4),
 // wave tile 64 x 96 or 128 x 64 made of 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16 (on gfx950 this form
-// sustains far more of the bf16 peak than 16 x 16 x 32). K advances 64 at a
+// v_mfma_f32_32x32x16_bf16 (measured faster in these kernels than 16 x 16 x 32,
+// although with register operands alone the 16 x 16 form issues a little
+// faster). K advances 64 at a
 // time through two-buffer LDS rings for the E and W tiles, filled by direct
 // global->LDS loads (global_load_lds_dwordx4: a lane moves 16 bytes, a wave
 // writes 1 KiB of LDS per instruction; the address is an SGPR base plus a
@@ -31,15 +32,10 @@
 // Epilogue: the accumulators are staged through LDS a pass of rows at a
 // time (one 16-byte LDS write per four columns) and leave as 16-byte row
 // stores; passes synchronise on LDS only (the stores are never waited for);
-// the bf16 input tile (residual x, or h) is fetched once before the first
-// store; bf16 packing is one v_cvt_pk_bf16_f32 per pair. Two epilogues: the
-// scalar gate (PageGram §3.1: out = x + g W_V e) and pass 1 of the Engram
-// fusion (Engram notes §3.3-3.4):
-// v = W_V e is stored in bf16 and, per token and 256-column block, the
-// partial sums RMSNorm and the context gate need (sum v^2; per branch sum
-// k^2, sum gamma_h gamma_k h k, sum h^2) go to the workspace, so k is never
-// stored. (Pass 1 on bf16 operands runs on the slot-ring kernel of
-// gemm_slots.hip; this kernel's Engram epilogue serves the E4M3 operands.)
+// the bf16 residual tile is fetched once before the first store; bf16
+// packing is one v_cvt_pk_bf16_f32 per pair. Two epilogues: the scalar gate
+// (PageGram §3.1: out = x + g W_V e) and fp32 output (the backward's GEMMs).
+// Pass 1 of the Engram fusion runs on the slot-ring kernel of gemm_slots.hip.
 //
 // Fallback kernel (K a multiple of 8): 128 x 128 tile, BK = 64, register-
 // staged double buffer; scalar gate only.
@@ -60,27 +56,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kColBlock = 256;   // Engram partial-sum column block
 constexpr int kPipeBK = 64;      // K stage of the pipelined kernel (bf16 elements)
 constexpr int kPipeBK8 = 128;    // the same 128 bytes per row in FP8 elements
 constexpr int kPipeStages = 2;   // its LDS ring
 
-enum { EPI_SCALAR = 0, EPI_ENGRAM = 1, EPI_F32 = 2 };
+enum { EPI_SCALAR = 0, EPI_F32 = 2 };
 
 struct EpiArgs {
   // scalar gate
   float g;
   const uint16_t* resid;   // [M][N] or NULL
   uint16_t* out;           // [M][N]
-  // Engram pass 1
-  int d;
-  int n_cb;                // d / 256 column blocks per segment
-  const uint16_t* h;       // [Mbr][M][d]
-  uint16_t* v;             // [M][d]
-  float* part_v;           // [n_cb][M]
-  float* part_k;           // [Mbr][3][n_cb][M]
-  const float* gamma_h;
-  const float* gamma_k;
   // fp32 output (g * acc): out_f32[row * ldo + col]; with split K, block
   // column blockIdx.y covers K range [y K, (y+1) K) of the operands and
   // writes its partial product at out_f32 + y * M * ldo
@@ -241,7 +227,6 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32 x 32 MFMA tiles per wave");
   static_assert(L < 64, "vmcnt range");
   static_assert(Cfg::kLdsBytes <= 160 * 1024, "LDS");
-  static_assert(EPI != EPI_ENGRAM || BN == kColBlock, "an Engram tile is one column block");
   static_assert(!GATHER || (!F8 && BKB == 128 && EPI == EPI_SCALAR && S == 2 && NT >= BM),
                 "fused gather: bf16 64-element rows, scalar gate");
 
@@ -284,17 +269,11 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
     pre_src = ep.resid;
     pre_ld = N;
     pre_c0 = n0;
-  } else if constexpr (EPI == EPI_F32) {
+  } else {
     pre_ok = false;
     pre_src = nullptr;
     pre_ld = 0;
     pre_c0 = 0;
-  } else {
-    const int seg = n0 / ep.d;
-    pre_ok = seg > 0;
-    pre_src = seg > 0 ? ep.h + (int64_t)(seg - 1) * M * ep.d : ep.h;
-    pre_ld = ep.d;
-    pre_c0 = n0 - seg * ep.d;
   }
 
   // Swizzle of the 16-byte chunk position within a row. gfx950's LDS serves
@@ -581,16 +560,6 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
     asm volatile("" ::: "memory");
   };
   load_pre(PRE_EARLY, NP * ITEMS);
-  // Engram: this thread's 8 columns are the same in every item (CPR divides
-  // the thread count), so the gain products are read once.
-  float gg[8];
-  if constexpr (EPI == EPI_ENGRAM) {
-    static_assert(NT % CPR == 0, "every item of a thread has the same columns");
-    const int seg = n0 / ep.d;
-    const int c = n0 - seg * ep.d + (tid % CPR) * 8;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) gg[u] = seg > 0 ? ep.gamma_h[c + u] * ep.gamma_k[c + u] : 0.f;
-  }
   // Pass p: the accumulator rows [p R, p R + R) of the block tile go to LDS.
   auto stage = [&](int p) {
     lds_barrier();
@@ -692,68 +661,6 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
             const int64_t o = row * N + col + u;
             const float x = ep.resid ? bf16_to_f32(ep.resid[o]) : 0.f;
             ep.out[o] = (uint16_t)pack_bf16x2(x + ep.g * y[u], 0.f);
-          }
-        }
-      }
-    }
-  } else {
-    // Engram pass 1: the block's 256 columns are one partial-sum column block
-    // of one segment (BN = 256 divides d); the 32 consecutive lanes of a row
-    // hold it. Edge tiles (rows past M) read h per item.
-    const int seg = n0 / ep.d;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      stage(p);
-#pragma unroll
-      for (int it = 0; it < ITEMS; ++it) {
-        const int idx = tid + it * NT;
-        const int c8 = (idx % CPR) * 8;
-        const int64_t row = m0 + p * R + idx / CPR;
-        const int c = n0 + c8 - seg * ep.d;
-        const bool live = row < M;
-        float y[8], xin[8];
-        item_y(p, it, y, xin);
-        if (!full && seg > 0 && live) {
-          const uint4 pr = *reinterpret_cast<const uint4*>(pre_src + row * pre_ld + pre_c0 + c8);
-          const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            xin[2 * u] = bf16_to_f32((uint16_t)(pw[u] & 0xFFFFu));
-            xin[2 * u + 1] = bf16_to_f32((uint16_t)(pw[u] >> 16));
-          }
-        }
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-        if (seg == 0) {
-          uint32_t vw[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) vw[u] = pack_bf16x2(y[2 * u], y[2 * u + 1]);
-          if (live)
-            *reinterpret_cast<uint4*>(ep.v + row * ep.d + c) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) s0 += y[u] * y[u];
-        } else {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            s0 += y[u] * y[u];
-            s1 += gg[u] * xin[u] * y[u];
-            s2 += xin[u] * xin[u];
-          }
-        }
-#pragma unroll
-        for (int sh = 1; sh < CPR; sh <<= 1) {
-          s0 += __shfl_xor(s0, sh, 64);
-          s1 += __shfl_xor(s1, sh, 64);
-          s2 += __shfl_xor(s2, sh, 64);
-        }
-        if (live && (lane % CPR) == 0) {
-          const int cb = c / kColBlock;
-          if (seg == 0) {
-            ep.part_v[(int64_t)cb * M + row] = s0;
-          } else {
-            float* pk = ep.part_k + (int64_t)(seg - 1) * 3 * ep.n_cb * M;
-            pk[((int64_t)0 * ep.n_cb + cb) * M + row] = s0;
-            pk[((int64_t)1 * ep.n_cb + cb) * M + row] = s1;
-            pk[((int64_t)2 * ep.n_cb + cb) * M + row] = s2;
           }
         }
       }
@@ -1040,30 +947,15 @@ hipError_t launch_gemm_f32(const void* A, int lda, const void* B, int ldb, int64
 }
 
 // Engram pass 1 (E % 64 == 0 and d % 256 == 0, checked by the caller; E %
-// 128 == 0 for FP8 operands, f8 = 1 with scales se, sw). bf16 operands go to
-// the slot-ring kernel, E4M3 operands to the pipelined kernel above.
+// 128 == 0 for FP8 operands, f8 = 1 with scales se, sw): the slot-ring
+// kernel of gemm_slots.hip for both operand types.
 hipError_t launch_engram_pass1(const void* e, int64_t N, int64_t E, const void* W,
                                int64_t d, int64_t Mbr, const void* h,
                                const float* gamma_h, const float* gamma_k, uint16_t* v,
                                float* part_v, float* part_k, int f8, int se, int sw,
                                hipStream_t s) {
-  EpiArgs ep{};
-  ep.d = (int)d;
-  ep.n_cb = (int)(d / kColBlock);
-  ep.h = static_cast<const uint16_t*>(h);
-  ep.v = v;
-  ep.part_v = part_v;
-  ep.part_k = part_k;
-  ep.gamma_h = gamma_h;
-  ep.gamma_k = gamma_k;
-  if (f8) {
-    ep.f8_sa = 127 - sw;
-    ep.f8_sb = 127 - se;
-    return launch_pipe<256, 256, kPipeBK8, kPipeStages, 1, EPI_ENGRAM, 2, 4, true>(
-        e, N, (int)((1 + Mbr) * d), (int)E, W, ep, s);
-  }
   return launch_engram_pass1_slots(e, N, E, W, d, Mbr, h, gamma_h, gamma_k, v, part_v, part_k,
-                                   s);
+                                   f8, se, sw, s);
 }
 
 }  // namespace pg

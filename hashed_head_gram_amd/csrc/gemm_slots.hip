@@ -1,23 +1,27 @@
-// Pass 1 of the Engram fusion on bf16 operands (gfx950): the fused projection
+// Pass 1 of the Engram fusion (gfx950): the fused projection
 // [W_V; W_K^(1..M)] e with its partial-sum epilogue (Engram notes §3.3-3.4:
 // v = W_V e is kept, k^m = W_K^m e only enters RMSNorm(k) and the context
 // gate's dot product with RMSNorm(h), so per token and 256-column block the
 // epilogue leaves sum v^2 and, per branch, sum k^2, sum gamma_h gamma_k h k
-// and sum h^2; v goes out in bf16).
+// and sum h^2; v goes out in bf16), on bf16 operands or on E4M3 ones with
+// power-of-two scales (the FP8 GEMM the Engram notes §3.4 name).
 //
 // Y[M x N] = E[M x K] . W[N x K]^T, 256 x 256 block tiles, 512 threads = 8
 // waves (two per SIMD) in a 2 x 4 grid of 128 x 64 wave tiles made of
-// v_mfma_f32_32x32x16_bf16 blocks (W fragment as the A operand, so a lane's
-// accumulators are runs of four consecutive output columns of one token).
+// 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16, or
+// v_mfma_scale_f32_32x32x64_f8f6f4 whose E8M0 operand scales undo the
+// operands' scaling); the W fragment is the A operand, so a lane's
+// accumulators are runs of four consecutive output columns of one token.
 //
-// K is walked in 32-element slots through a ring of four LDS slot buffers
-// (16 KB of E rows and 16 KB of W rows each), filled by direct global->LDS
-// loads (global_load_lds_dwordx4). The DMA of slot s + 4 goes into slot s's
-// buffer as soon as every wave has read slot s, two instructions per wave and
-// K step, spread over two K steps, so three slots of loads stay in flight and
-// no wave's issue stalls behind a burst of them. Fragments are read one K
-// step ahead; one block barrier per slot, in its middle, marks the next slot
-// as landed and the current slot's buffer as free.
+// K is walked in slots of 64 bytes per row (32 bf16 or 64 E4M3 elements)
+// through a ring of four LDS slot buffers (16 KB of E rows and 16 KB of W
+// rows each), filled by direct global->LDS loads (global_load_lds_dwordx4).
+// The DMA of slot s + 4 goes into slot s's buffer as soon as every wave has
+// read slot s, so three slots of loads stay in flight. bf16: two K steps per
+// slot, fragments read one step ahead, the slot's DMA spread over its two
+// steps and one block barrier per slot in its middle. E4M3: one K step per
+// slot, the barrier at its start, the next slot's fragments read between
+// the MFMAs into a second fragment set.
 //
 // Epilogue without an accumulator round trip: as the last four slots' buffers
 // free up, their DMA turns to the h tile of the block's branch (a quarter of
@@ -35,6 +39,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -72,13 +77,17 @@ struct SlotEpi {
   float* part_k;           // [Mbr][3][n_cb][M]
   const float* gamma_h;
   const float* gamma_k;
+  int f8_sa, f8_sb;        // E8M0 operand scales of the E4M3 form (W, e)
 };
 
+template <bool F8>
 __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __restrict__ E,
                                                              const uint8_t* __restrict__ W,
                                                              int64_t M, int N, int K,
                                                              SlotEpi ep) {
-  constexpr int BM = 256, BN = 256, SK = 32, EB = 2, SKB = SK * EB, NSLOT = 4;
+  // a slot is 64 bytes of every row: 32 bf16 or 64 E4M3 K elements
+  constexpr int EB = F8 ? 1 : 2, SK = 64 / EB;
+  constexpr int BM = 256, BN = 256, SKB = SK * EB, NSLOT = 4;
   constexpr int NT = 512, NW = 8, WGN = 4;
   constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
   constexpr int LPR = SKB / 16, RPI = 64 / LPR, ROWS_PER_LINE = 256 / SKB;
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   const bool use_h = seg > 0;
   const uint16_t* hsrc = use_h ? ep.h + (int64_t)(seg - 1) * M * ep.d : ep.h;
   const bool early_h = use_h && full;
-  const int KS = K / SK;                   // slots (K a multiple of 64: KS even)
+  const int KS = K / SK;                   // slots (an even count: K a multiple of 2 SK)
 
   // Chunk c of a slot row r sits at c ^ swz(r): the 16 lanes a 16-byte read
   // serves together hit 16 distinct 16-byte slots of a 256-byte line.
@@ -215,77 +224,151 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // v_mfma_f32_32x32x16_bf16: lane l holds operand row l % 32 and K elements
-  // 8 (l / 32) .. +7 of the step; D element q of lane l is row 8 (q / 4) +
-  // 4 (l / 32) + q % 4 (an output column), column l % 32 (a token).
-  const int fr = lane & 31;
-  bf16x8_t fa[2][FM], fb[2][FN];
-  auto load_step = [&](int s, int t, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
-    const int b = s & 3;
-    const uint8_t* se = smem + b * kSlotE;
-    const uint8_t* sw = smem + kWOff + b * kSlotW;
-    const int c = t * 2 + (lane >> 5);
+  if constexpr (F8) {
+    // v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds operand row l % 32 and K
+    // elements 32 (l / 32) .. +31 of the slot (two 16-byte chunks); D as for
+    // the bf16 form. One MFMA K step per slot: barrier B_s at the slot's start
+    // (slot s + 1 landed everywhere, every read of slot s done), period s's
+    // loads into slot s's buffer, then slot s's MFMAs with slot s + 1's
+    // fragment reads between them, into the other of two fragment sets (the
+    // loop runs two slots per iteration, so the set is a constant). The last
+    // slot also reads the next buffer; those values are never used.
+    const int fr = lane & 31;
+    i32x8_t fa[2][FM], fb[2][FN];
+    auto read8 = [&](const uint8_t* rowp, int r) -> i32x8_t {
+      const int c0 = 2 * (lane >> 5);
+      const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((c0 ^ swz(r)) * 16));
+      const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((c0 + 1) ^ swz(r)) * 16));
+      return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_slot = [&](int s, i32x8_t (&af)[FM], i32x8_t (&bf)[FN]) {
+      const uint8_t* se = smem + (s & 3) * kSlotE;
+      const uint8_t* sw = smem + kWOff + (s & 3) * kSlotW;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * WTM + i * 32 + fr;
-      af[i] = __builtin_bit_cast(bf16x8_t,
-                                 *reinterpret_cast<const uint4*>(se + r * SKB + ((c ^ swz(r)) * 16)));
-    }
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + fr;
+        af[i] = read8(se + r * SKB, r);
+      }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * WTN + j * 32 + fr;
-      bf[j] = __builtin_bit_cast(bf16x8_t,
-                                 *reinterpret_cast<const uint4*>(sw + r * SKB + ((c ^ swz(r)) * 16)));
-    }
-  };
-  auto mma_step = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bf)[FN], bool reads) {
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + fr;
+        bf[j] = read8(sw + r * SKB, r);
+      }
+    };
+    auto f8_slot = [&](int s, i32x8_t (&af)[FM], i32x8_t (&bf)[FN], i32x8_t (&an)[FM],
+                       i32x8_t (&bnx)[FN]) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < KS) wait_slot(s + 1, s);
+      lgkm0();
+      bar();
+      issue_half(s, 0);
+      issue_half(s, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_slot(s + 1, an, bnx);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    // the step's fragment reads go out one after each of its first MFMAs
-    if (reads) {
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bf[j], af[i], acc[i][j], 0, 0, 0, ep.f8_sa, 0, ep.f8_sb);
+      // two 16-byte reads after each of the first six MFMAs
 #pragma unroll
       for (int x = 0; x < FM + FN; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-    }
-  };
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // prologue: periods -4 .. -1 (slots 0-3); slot 0 landed; its step 0 read
+    // prologue: periods -4 .. -1 (slots 0-3); slot 0 landed; its fragments read
 #pragma unroll
-  for (int p = -4; p < 0; ++p) {
-    issue_half(p, 0);
-    issue_half(p, 1);
-  }
-  wait_slot(0, 0);
-  bar();
-  load_step(0, 0, fa[0], fb[0]);
-
-  // Step (s, 0): reads of (s, 1), MFMAs of (s, 0), the second half of period
-  // s - 1. Barrier B_s: slot s + 1 has landed everywhere and slot s is read.
-  // Step (s, 1): the first half of period s, reads of (s + 1, 0), MFMAs.
-  for (int s = 0; s < KS; ++s) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (s > 0) issue_half(s - 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_step(s, 1, fa[1], fb[1]);
-    mma_step(fa[0], fb[0], true);
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < KS) wait_slot(s + 1, s);
-    lgkm0();
+    for (int p = -4; p < 0; ++p) {
+      issue_half(p, 0);
+      issue_half(p, 1);
+    }
+    wait_slot(0, 0);
     bar();
-    issue_half(s, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool rd = s + 1 < KS;
-    if (rd) load_step(s + 1, 0, fa[0], fb[0]);
-    mma_step(fa[1], fb[1], rd);
-    __builtin_amdgcn_sched_barrier(0);
+    read_slot(0, fa[0], fb[0]);
+    for (int s = 0; s < KS; s += 2) {
+      f8_slot(s, fa[0], fb[0], fa[1], fb[1]);
+      f8_slot(s + 1, fa[1], fb[1], fa[0], fb[0]);
+    }
+  } else {
+
+    // v_mfma_f32_32x32x16_bf16: lane l holds operand row l % 32 and K elements
+    // 8 (l / 32) .. +7 of the step; D element q of lane l is row 8 (q / 4) +
+    // 4 (l / 32) + q % 4 (an output column), column l % 32 (a token).
+    const int fr = lane & 31;
+    bf16x8_t fa[2][FM], fb[2][FN];
+    auto load_step = [&](int s, int t, bf16x8_t (&af)[FM], bf16x8_t (&bf)[FN]) {
+      const int b = s & 3;
+      const uint8_t* se = smem + b * kSlotE;
+      const uint8_t* sw = smem + kWOff + b * kSlotW;
+      const int c = t * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + fr;
+        af[i] = __builtin_bit_cast(bf16x8_t,
+                                   *reinterpret_cast<const uint4*>(se + r * SKB + ((c ^ swz(r)) * 16)));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + fr;
+        bf[j] = __builtin_bit_cast(bf16x8_t,
+                                   *reinterpret_cast<const uint4*>(sw + r * SKB + ((c ^ swz(r)) * 16)));
+      }
+    };
+    auto mma_step = [&](const bf16x8_t (&af)[FM], const bf16x8_t (&bf)[FN], bool reads) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      // the step's fragment reads go out one after each of its first MFMAs
+      if (reads) {
+#pragma unroll
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+    };
+
+    // prologue: periods -4 .. -1 (slots 0-3); slot 0 landed; its step 0 read
+#pragma unroll
+    for (int p = -4; p < 0; ++p) {
+      issue_half(p, 0);
+      issue_half(p, 1);
+    }
+    wait_slot(0, 0);
+    bar();
+    load_step(0, 0, fa[0], fb[0]);
+
+    // Step (s, 0): reads of (s, 1), MFMAs of (s, 0), the second half of period
+    // s - 1. Barrier B_s: slot s + 1 has landed everywhere and slot s is read.
+    // Step (s, 1): the first half of period s, reads of (s + 1, 0), MFMAs.
+    for (int s = 0; s < KS; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s > 0) issue_half(s - 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(s, 1, fa[1], fb[1]);
+      mma_step(fa[0], fb[0], true);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < KS) wait_slot(s + 1, s);
+      lgkm0();
+      bar();
+      issue_half(s, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool rd = s + 1 < KS;
+      if (rd) load_step(s + 1, 0, fa[0], fb[0]);
+      mma_step(fa[1], fb[1], rd);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    issue_half(KS - 1, 1);
   }
-  issue_half(KS - 1, 1);
 
   // ---- epilogue
   auto lds_barrier = [] {
@@ -433,12 +516,14 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
 
 }  // namespace
 
-// Pass 1 on bf16 operands: e [N][E], W [(1 + Mbr) d][E] (E a multiple of 64,
-// d of 256; checked by the caller).
+// Pass 1: e [N][E], W [(1 + Mbr) d][E], bf16 (E a multiple of 64) or, with
+// f8, E4M3 with power-of-two scales 2^se (e) and 2^sw (W) (E a multiple of
+// 128); d a multiple of 256 (checked by the caller).
 hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const void* W,
                                      int64_t d, int64_t Mbr, const void* h,
                                      const float* gamma_h, const float* gamma_k, uint16_t* v,
-                                     float* part_v, float* part_k, hipStream_t s) {
+                                     float* part_v, float* part_k, int f8, int se, int sw,
+                                     hipStream_t s) {
   SlotEpi ep{};
   ep.d = (int)d;
   ep.n_cb = (int)(d / kColBlock);
@@ -448,11 +533,18 @@ hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const 
   ep.part_k = part_k;
   ep.gamma_h = gamma_h;
   ep.gamma_k = gamma_k;
+  ep.f8_sa = 127 - sw;
+  ep.f8_sb = 127 - se;
   const int64_t Nout = (1 + Mbr) * d;
   const int64_t blocks = ((N + 255) / 256) * ((Nout + 255) / 256);
-  hipLaunchKernelGGL(engram_slot_kernel, dim3((unsigned)blocks), dim3(512), 0, s,
-                     static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
-                     (int)Nout, (int)E, ep);
+  if (f8)
+    hipLaunchKernelGGL(engram_slot_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, s,
+                       static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
+                       (int)Nout, (int)E, ep);
+  else
+    hipLaunchKernelGGL(engram_slot_kernel<false>, dim3((unsigned)blocks), dim3(512), 0, s,
+                       static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
+                       (int)Nout, (int)E, ep);
   return hipGetLastError();
 }
 
