@@ -355,8 +355,7 @@ __device__ __forceinline__ void pipe_body(const uint8_t* __restrict__ A,
 
   // v_mfma_f32_32x32x16_bf16: lane l holds A row l % 32 (B column l % 32),
   // K elements 8 (l / 32) .. +7 of the 16; D element q of lane l is row
-  // 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32. (On gfx950 this form
-  // sustains far more of the bf16 peak than the 16 x 16 x 32 one.) The W
+  // 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32. The W
   // fragment goes in as A and the E fragment as B, so D is the transposed
   // tile: lane l holds token row l % 32 and, per q / 4, the four consecutive
   // output columns 8 (q / 4) + 4 (l / 32) + 0..3 -- contiguous in memory.
