@@ -164,6 +164,12 @@ FWD_CASES = {
     "engram_r32_ragged": small_wl(4, K=4, r=32, head_rows=[101, 103, 107, 109, 113, 127, 131,
                                                            137], B=2, T=45, d=256, M=2,
                                   gamma="random"),
+    # e_dim 128: two 64-element K slots, so the h tile's first quarters are
+    # requested with the first slots; 600 tokens (a ragged third row tile),
+    # d = 512, three branches
+    "engram_E128_two_slots": small_wl(4, K=4, r=16, head_rows=[101, 103, 107, 109, 113, 127,
+                                                               131, 137], B=2, T=300, d=512,
+                                      M=3, gamma="random"),
 }
 
 

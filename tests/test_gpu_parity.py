@@ -194,6 +194,11 @@ RAGGED = {
                                      pages=[5, 7, 11, 13], B=2, T=50, d=64),
     "bf16_nosigns_T1": small_wl(1, use_signs=0, pages=[7, 7], B=5, T=1, d=128),
     "bf16_engram_T2": small_wl(2, B=4, T=2, d=64),
+    # e_dim 64: two 32-element K slots of the fused projection (the h tile's
+    # first quarters are requested with the first slots); 600 tokens, d = 512,
+    # three branches
+    "bf16_engram_E64_two_slots": small_wl(4, K=2, r=16, head_rows=[101, 103, 107, 109], B=2,
+                                          T=300, d=512, M=3, gamma="random"),
 }
 
 
