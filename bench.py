@@ -212,19 +212,20 @@ def read_bytes_by_size(rdreq_csv):
     return out
 
 
-def write_traffic(workload, fetch_csv, write_csv, rdreq_csv=None):
+def write_traffic(workload, fetch_csv, write_csv, rdreq_csv=None, path=None):
     """HBM bytes per launch of the gather and projection kernels (and of the
     gathered projection where the workload runs it): FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
     1 GiB device copy read and write exactly 1 GiB. With rdreq_csv, read bytes
     also from the read requests by size, unscaled, next to the copy's reading
-    of the same counters (which should be 1 GiB)."""
+    of the same counters (which should be 1 GiB). The record goes into path
+    (profiles/traffic.json by default), replacing the workload's entry."""
     fetch = counter_means(fetch_csv, "FETCH_SIZE")
     write = counter_means(write_csv, "WRITE_SIZE")
     by_size = read_bytes_by_size(rdreq_csv) if rdreq_csv else {}
     f_scale = COPY_BYTES / (fetch["copy"] * 1024)
     w_scale = COPY_BYTES / (write["copy"] * 1024)
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
     for stage in ("gather", "projection", "gathered", "pass1", "pass2"):
