@@ -21,7 +21,10 @@
 // slot, fragments read one step ahead, the slot's DMA spread over its two
 // steps and one block barrier per slot in its middle. E4M3: one K step per
 // slot, the barrier at its start, the next slot's fragments read between
-// the MFMAs into a second fragment set.
+// the MFMAs into a second fragment set. Away from the first and last slots
+// every DMA period loads a K slot, so those slots run a branch-free body:
+// constant vmcnt waits, and the MFMAs after a barrier start before that
+// period's DMA is issued.
 //
 // Epilogue without an accumulator round trip: as the last four slots' buffers
 // free up, their DMA turns to the h tile of the block's branch (a quarter of
@@ -33,6 +36,8 @@
 // The h tile's and the v staging's 16-byte chunks sit at chunk ^ (row & 31)
 // so a half-wave's reads of one column block hit distinct banks.
 #include "common.h"
+
+#include <type_traits>
 
 namespace pg {
 namespace {
@@ -193,6 +198,21 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
       }
     }
   };
+  // issue_half for a period that loads a K slot (s + 4 < KS): no branch
+  auto issue_slot_half = [&](int p, int half) {
+    const int s = p + 4, b = s & 3;
+    if (half == 0) {
+      const uint8_t* base = E + (rbE * K + (int64_t)s * SK) * EB;
+      const uint32_t l = lds0 + b * kSlotE + wave * E_DMA * 1024;
+      dma16(base, offE[0], l);
+      dma16(base, offE[1], l + 1024);
+    } else {
+      const uint8_t* base = W + (rbW * K + (int64_t)s * SK) * EB;
+      const uint32_t l = lds0 + kWOff + b * kSlotW + wave * W_DMA * 1024;
+      dma16(base, offW[0], l);
+      dma16(base, offW[1], l + 1024);
+    }
+  };
   // this wave's loads of slot s have landed when only those of the periods
   // after the one that issued it (s - 4), up to p_now - 1, are outstanding
   auto wait_slot = [&](int s, int p_now) {
@@ -256,29 +276,59 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
         bf[j] = read8(sw + r * SKB, r);
       }
     };
+    auto f8_mma = [&](int i, int j, const i32x8_t (&af)[FM], const i32x8_t (&bf)[FN]) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0, 0,
+                                                                   0, ep.f8_sa, 0, ep.f8_sb);
+    };
+    // kSteady: slot s + 1 exists and periods s - 2 .. s all load K slots, so
+    // the wait is a constant and the slot's MFMAs start right after the
+    // barrier, its DMA going out behind the first one
     auto f8_slot = [&](int s, i32x8_t (&af)[FM], i32x8_t (&bf)[FN], i32x8_t (&an)[FM],
-                       i32x8_t (&bnx)[FN]) {
+                       i32x8_t (&bnx)[FN], auto steady) {
+      constexpr bool kSteady = decltype(steady)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < KS) wait_slot(s + 1, s);
+      if constexpr (kSteady)
+        wait_vm<2 * LS>();
+      else if (s + 1 < KS)
+        wait_slot(s + 1, s);
       lgkm0();
       bar();
-      issue_half(s, 0);
-      issue_half(s, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      read_slot(s + 1, an, bnx);
+      if constexpr (kSteady) {
+        f8_mma(0, 0, af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_slot_half(s, 0);
+        issue_slot_half(s, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_slot(s + 1, an, bnx);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              bf[j], af[i], acc[i][j], 0, 0, 0, ep.f8_sa, 0, ep.f8_sb);
-      // two 16-byte reads after each of the first six MFMAs
+          for (int j = 0; j < FN; ++j)
+            if (i + j > 0) f8_mma(i, j, af, bf);
+        // two 16-byte reads before each of the next six MFMAs
 #pragma unroll
-      for (int x = 0; x < FM + FN; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 1 - (FM + FN), 0);
+      } else {
+        issue_half(s, 0);
+        issue_half(s, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_slot(s + 1, an, bnx);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) f8_mma(i, j, af, bf);
+        // two 16-byte reads after each of the first six MFMAs
+#pragma unroll
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -291,9 +341,16 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
     wait_slot(0, 0);
     bar();
     read_slot(0, fa[0], fb[0]);
-    for (int s = 0; s < KS; s += 2) {
-      f8_slot(s, fa[0], fb[0], fa[1], fb[1]);
-      f8_slot(s + 1, fa[1], fb[1], fa[0], fb[0]);
+    using steady_t = std::integral_constant<bool, true>;
+    using generic_t = std::integral_constant<bool, false>;
+    int s = 0;
+    for (; s + 5 < KS; s += 2) {
+      f8_slot(s, fa[0], fb[0], fa[1], fb[1], steady_t{});
+      f8_slot(s + 1, fa[1], fb[1], fa[0], fb[0], steady_t{});
+    }
+    for (; s < KS; s += 2) {
+      f8_slot(s, fa[0], fb[0], fa[1], fb[1], generic_t{});
+      f8_slot(s + 1, fa[1], fb[1], fa[0], fb[0], generic_t{});
     }
   } else {
 
@@ -350,23 +407,62 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
     // Step (s, 0): reads of (s, 1), MFMAs of (s, 0), the second half of period
     // s - 1. Barrier B_s: slot s + 1 has landed everywhere and slot s is read.
     // Step (s, 1): the first half of period s, reads of (s + 1, 0), MFMAs.
-    for (int s = 0; s < KS; ++s) {
+    // kSteady (0 < s < KS - 4): both DMA periods of the slot load K slots
+    // and slot s + 1 exists, so the wait is a constant, nothing branches, and
+    // step (s, 1) starts its MFMAs right after the barrier with the period's
+    // DMA behind the first one.
+    auto slot = [&](int s, auto steady) {
+      constexpr bool kSteady = decltype(steady)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (s > 0) issue_half(s - 1, 1);
+      if constexpr (kSteady)
+        issue_slot_half(s - 1, 1);
+      else if (s > 0)
+        issue_half(s - 1, 1);
       __builtin_amdgcn_sched_barrier(0);
       load_step(s, 1, fa[1], fb[1]);
       mma_step(fa[0], fb[0], true);
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < KS) wait_slot(s + 1, s);
+      if constexpr (kSteady)
+        wait_vm<2 * LS>();
+      else if (s + 1 < KS)
+        wait_slot(s + 1, s);
       lgkm0();
       bar();
-      issue_half(s, 0);
+      if constexpr (kSteady) {
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][0], fa[1][0], acc[0][0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_slot_half(s, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(s + 1, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (i + j > 0)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+        // one read before each of the next six MFMAs
+#pragma unroll
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 1 - (FM + FN), 0);
+      } else {
+        issue_half(s, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool rd = s + 1 < KS;
+        if (rd) load_step(s + 1, 0, fa[0], fb[0]);
+        mma_step(fa[1], fb[1], rd);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      const bool rd = s + 1 < KS;
-      if (rd) load_step(s + 1, 0, fa[0], fb[0]);
-      mma_step(fa[1], fb[1], rd);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    using steady_t = std::integral_constant<bool, true>;
+    using generic_t = std::integral_constant<bool, false>;
+    slot(0, generic_t{});
+    int s = 1;
+    for (; s < KS - 4; ++s) slot(s, steady_t{});
+    for (; s < KS; ++s) slot(s, generic_t{});
     issue_half(KS - 1, 1);
   }
 
