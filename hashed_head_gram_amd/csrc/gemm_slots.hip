@@ -24,7 +24,9 @@
 // the MFMAs into a second fragment set. Away from the first and last slots
 // every DMA period loads a K slot, so those slots run a branch-free body:
 // constant vmcnt waits, and the MFMAs after a barrier start before that
-// period's DMA is issued.
+// period's DMA is issued. Each tile starts its walk over K at slot
+// (bm + bn) mod KS, so the tiles sharing a panel ask for each slot a slot
+// period apart instead of all at once (the sum order over K differs per tile).
 //
 // Epilogue without an accumulator round trip: as the last four slots' buffers
 // free up, their DMA turns to the h tile of the block's branch (a quarter of
@@ -131,6 +133,12 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   const uint16_t* hsrc = use_h ? ep.h + (int64_t)(seg - 1) * M * ep.d : ep.h;
   const bool early_h = use_h && full;
   const int KS = K / SK;                   // slots (an even count: K a multiple of 2 SK)
+  // The tiles that share an E panel (same bm) or a W panel (same bn) walk K
+  // from different starting slots, one apart, so that of the tiles running
+  // together only the first to ask for a panel's slot misses in L2 and the
+  // others find it there a slot period later.
+  const int s0 = (int)((bm + bn) % KS);
+  auto phys = [&](int s) -> int64_t { return s + s0 < KS ? s + s0 : s + s0 - KS; };
 
   // Chunk c of a slot row r sits at c ^ swz(r): the 16 lanes a 16-byte read
   // serves together hit 16 distinct 16-byte slots of a 256-byte line.
@@ -175,12 +183,12 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
     if (s < KS) {
       const int b = s & 3;
       if (half == 0) {
-        const uint8_t* base = E + (rbE * K + (int64_t)s * SK) * EB;
+        const uint8_t* base = E + (rbE * K + phys(s) * SK) * EB;
         const uint32_t l = lds0 + b * kSlotE + wave * E_DMA * 1024;
         dma16(base, offE[0], l);
         dma16(base, offE[1], l + 1024);
       } else {
-        const uint8_t* base = W + (rbW * K + (int64_t)s * SK) * EB;
+        const uint8_t* base = W + (rbW * K + phys(s) * SK) * EB;
         const uint32_t l = lds0 + kWOff + b * kSlotW + wave * W_DMA * 1024;
         dma16(base, offW[0], l);
         dma16(base, offW[1], l + 1024);
@@ -202,12 +210,12 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   auto issue_slot_half = [&](int p, int half) {
     const int s = p + 4, b = s & 3;
     if (half == 0) {
-      const uint8_t* base = E + (rbE * K + (int64_t)s * SK) * EB;
+      const uint8_t* base = E + (rbE * K + phys(s) * SK) * EB;
       const uint32_t l = lds0 + b * kSlotE + wave * E_DMA * 1024;
       dma16(base, offE[0], l);
       dma16(base, offE[1], l + 1024);
     } else {
-      const uint8_t* base = W + (rbW * K + (int64_t)s * SK) * EB;
+      const uint8_t* base = W + (rbW * K + phys(s) * SK) * EB;
       const uint32_t l = lds0 + kWOff + b * kSlotW + wave * W_DMA * 1024;
       dma16(base, offW[0], l);
       dma16(base, offW[1], l + 1024);
