@@ -70,6 +70,10 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds));
 }
+// The same with 4 bytes per lane (the wave's 256 bytes to LDS address lds).
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(base), "{m0}"(lds));
+}
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
@@ -104,7 +108,8 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   constexpr int kWOff = NSLOT * kSlotE;
   constexpr int kRingBytes = NSLOT * (kSlotE + kSlotW);
   constexpr int kRedOff = kRingBytes;
-  constexpr int kLds = kRingBytes + WGN * BM * 3 * 4;
+  constexpr int kGamOff = kRedOff + WGN * BM * 3 * 4;   // gamma_h, gamma_k of the 256 columns
+  constexpr int kLds = kGamOff + 2 * BN * 4;
   static_assert(E_DMA == 2 && W_DMA == 2, "two DMA instructions per operand and slot");
   static_assert(kLds <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
@@ -115,16 +120,18 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   // Blocks are renumbered so that each XCD (blocks are dealt round-robin to
   // the 8 XCDs) runs a contiguous range of tiles, walked in groups of 8 M
   // tiles N-major: concurrent tiles share their E and W panels in one L2.
-  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  int64_t bid = blockIdx.x;
+  // (32-bit arithmetic: the tile counts fit, and 64-bit divisions by run-time
+  // values expand to long scalar sequences every wave would run)
+  const uint32_t nbm = (uint32_t)((M + BM - 1) / BM), nbn = (uint32_t)((N + BN - 1) / BN);
+  uint32_t bid = blockIdx.x;
   {
-    const int64_t total = nbm * nbn, per = total / 8;
+    const uint32_t total = nbm * nbn, per = total / 8;
     if (bid < per * 8) bid = (bid & 7) * per + (bid >> 3);
   }
-  const int64_t per_group = 8 * nbn, g = bid / per_group, local = bid - g * per_group;
-  const int64_t grows = nbm - g * 8 < 8 ? nbm - g * 8 : 8;
-  const int64_t bn = local / grows, bm = g * 8 + (local - bn * grows);
-  const int64_t m0 = bm * BM;
+  const uint32_t per_group = 8 * nbn, g = bid / per_group, local = bid - g * per_group;
+  const uint32_t grows = nbm - g * 8 < 8 ? nbm - g * 8 : 8;
+  const uint32_t bn = local / grows, bm = g * 8 + (local - bn * grows);
+  const int64_t m0 = (int64_t)bm * BM;
   const int n0 = (int)(bn * BN);
   const int seg = n0 / ep.d;               // 0: v, m >= 1: k of branch m
   const int cl0 = n0 - seg * ep.d;         // first column within the segment
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   // from different starting slots, one apart, so that of the tiles running
   // together only the first to ask for a panel's slot misses in L2 and the
   // others find it there a slot period later.
-  const int s0 = (int)((bm + bn) % KS);
+  const int s0 = (int)((bm + bn) % (uint32_t)KS);
   auto phys = [&](int s) -> int64_t { return s + s0 < KS ? s + s0 : s + s0 - KS; };
 
   // Chunk c of a slot row r sits at c ^ swz(r): the 16 lanes a 16-byte read
@@ -163,17 +170,19 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   uint32_t offE[2], offW[2];
   const int64_t rbE = dma_offsets(M, m0, offE);
   const int64_t rbW = dma_offsets(N, n0, offW);
-  // h tile row r (0..255): quarter r / 64 lives in the buffer of slot
-  // KS - 4 + r / 64 (E part rows 0-31, W part rows 32-63), 512 bytes a row
+  // h tile row r (0..255), 512 bytes a row: quarter q = (r / 32) & 3 holds
+  // the rows that the waves' epilogue step q reads (rows 32 q .. +31 in the E
+  // part of the buffer of slot KS - 4 + q, rows 128 + 32 q .. +31 in its W
+  // part), so the epilogue can start on the quarters that landed first.
   auto hrow_off = [&](int r) -> uint32_t {
-    const int b = (KS - 4 + (r >> 6)) & 3;
-    const int rr = r & 63;
-    return (uint32_t)(rr < 32 ? b * kSlotE + rr * 512 : kWOff + b * kSlotW + (rr - 32) * 512);
+    const int b = (KS - 4 + ((r >> 5) & 3)) & 3;
+    const int rr = r & 31;
+    return (uint32_t)(r < 128 ? b * kSlotE + rr * 512 : kWOff + b * kSlotW + rr * 512);
   };
   // DMA period p (issued between the barriers of slots p and p + 1; the
   // prologue is periods -4 .. -1) loads slot p + 4 into slot p's buffer, or,
-  // once the slots are out, quarter p + 4 - KS of the h tile; half 0 is the
-  // E rows (h rows 0-31 of the quarter), half 1 the W rows (h rows 32-63).
+  // once the slots are out, quarter q = p + 4 - KS of the h tile; half 0 is
+  // the E part (h rows 32 q .. +31), half 1 the W part (rows 128 + 32 q ..).
   auto period_count = [&](int p) -> int {
     const int s = p + 4;
     return (s < KS || (early_h && s - KS < 4)) ? LS : 0;
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
       }
     } else if (early_h && s - KS < 4) {
       // 32 rows: 4 per wave, 2 per instruction (lanes 0-31 and 32-63)
-      const int rw = (s - KS) * 64 + half * 32 + wave * 4;
+      const int rw = half * 128 + (s - KS) * 32 + wave * 4;
       const int p16 = lane & 31;
       const uint8_t* base = reinterpret_cast<const uint8_t*>(hsrc + (m0 + rw) * (int64_t)ep.d + cl0);
 #pragma unroll
@@ -251,6 +260,15 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // k tiles: gamma_h and gamma_k of the tile's 256 columns go to LDS by DMA
+  // ahead of the first slot (waves 0-3, 64 columns each), so the epilogue
+  // issues no global load and can wait on its h quarters one by one; the
+  // prologue's wait for slot 0 covers them
+  if (use_h && wave < 4) {
+    dma4(ep.gamma_h + cl0 + wave * 64, (uint32_t)lane * 4, lds0 + kGamOff + wave * 256);
+    dma4(ep.gamma_k + cl0 + wave * 64, (uint32_t)lane * 4, lds0 + kGamOff + BN * 4 + wave * 256);
+  }
 
   if constexpr (F8) {
     // v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds operand row l % 32 and K
@@ -485,19 +503,24 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
   float* red = reinterpret_cast<float*>(smem + kRedOff);   // [wn][256 rows][3]
   if (use_h) {
     // this lane's columns within the segment: cl0 + wn 64 + j 32 + 8 g4 + 4 hl + u
+    const float* gH = reinterpret_cast<const float*>(smem + kGamOff);
+    const float* gK = gH + BN;
     float gg[FN][4][4];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = cl0 + wn * WTN + j * 32 + 8 * g4 + 4 * hl + u;
-          gg[j][g4][u] = ep.gamma_h[c] * ep.gamma_k[c];
-        }
-    wait_vm<0>();
-    bar();   // every wave's h rows have landed; every slot has been read
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = wn * WTN + j * 32 + 8 * g4 + 4 * hl;
+        const float4 a = *reinterpret_cast<const float4*>(gH + c);
+        const float4 b = *reinterpret_cast<const float4*>(gK + c);
+        gg[j][g4][0] = a.x * b.x;
+        gg[j][g4][1] = a.y * b.y;
+        gg[j][g4][2] = a.z * b.z;
+        gg[j][g4][3] = a.w * b.w;
+      }
     if (!early_h) {
+      wait_vm<0>();
+      bar();   // every slot has been read
       // edge tile: h rows straight into the freed ring (zeros past M)
       for (int idx = tid; idx < BM * 32; idx += NT) {
         const int r = idx >> 5, c = idx & 31;
@@ -508,8 +531,18 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* __re
       }
       lds_barrier();
     }
+    static_assert(FM == 4, "one h quarter per row block");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (early_h) {
+        // quarter i (this wave's last 4 (3 - i) DMA instructions are later
+        // quarters) has landed from every wave
+        if (i == 0) wait_vm<12>();
+        if (i == 1) wait_vm<8>();
+        if (i == 2) wait_vm<4>();
+        if (i == 3) wait_vm<0>();
+        bar();
+      }
       const int rl = wm * WTM + i * 32 + (lane & 31);
       const uint8_t* hrow = smem + hrow_off(rl) + hl * 8;
       // this row block's accumulators, copied out of the accumulator registers
