@@ -30,13 +30,16 @@
 //
 // Epilogue without an accumulator round trip: as the last four slots' buffers
 // free up, their DMA turns to the h tile of the block's branch (a quarter of
-// the 256 x 256 bf16 tile each), so it is in LDS when the loop ends. Each lane
-// then forms its partial sums straight from its accumulators and the h values
-// of the same elements, one cross-lane add pairs the two half-waves holding a
-// token's columns, and the four column waves meet in a small LDS table. v
-// tiles go out through LDS as 16-byte row stores (the ring is free by then).
-// The h tile's and the v staging's 16-byte chunks sit at chunk ^ (row & 31)
-// so a half-wave's reads of one column block hit distinct banks.
+// the 256 x 256 bf16 tile each: quarter q holds the rows the waves handle in
+// epilogue step q), so it is in LDS as the loop ends, and each step waits
+// only for its own quarter. Each lane forms its partial sums straight from
+// its accumulators and the h values of the same elements, one cross-lane add
+// pairs the two half-waves holding a token's columns, and the four column
+// waves meet in a small LDS table; gamma_h and gamma_k of the tile's columns
+// come into LDS by DMA before the first slot. v tiles go out through LDS as
+// 16-byte row stores (the ring is free by then). The h tile's and the v
+// staging's 16-byte chunks sit at chunk ^ (row & 31) so a half-wave's reads
+// of one column block hit distinct banks.
 #include "common.h"
 
 #include <type_traits>
