@@ -282,6 +282,40 @@ def test_zero_table_leaves_residual(base):
     assert torch.equal(out.float(), c.resid.float())
 
 
+# The fused projection walks its tiles on one block per CU when E is a
+# multiple of 128 (each tile's epilogue loads the next tile's first slots):
+# about 1,000-1,600 tiles, so every block takes several, v and k tiles
+# follow one another, and the ragged last M tile sits in the walk's last
+# group, some of its k tiles with tiles after them. Outputs at tile edges,
+# in the ragged tile and at random positions against the oracle.
+TILE_WALK = {
+    "E1280_d512_M3_N51000": dict(K=8, r=80, head_rows=[211 + 2 * q for q in range(16)], B=3,
+                                 T=17000, d=512, M=3),
+    "E128_d256_M3_N64006": dict(K=4, r=16, head_rows=[101, 103, 107, 109, 113, 127, 131, 137],
+                                B=2, T=32003, d=256, M=3),
+}
+
+
+@pytest.mark.parametrize("name", list(TILE_WALK))
+def test_engram_fusion_tile_walk(name):
+    wl = small_wl(4, gamma="random", **TILE_WALK[name])
+    print(f"[tile walk] {name}", flush=True)
+    c = Case(wl)
+    out = c.run_forward()
+    torch.cuda.synchronize()
+    pos = set(sample_positions(c, n_random=64).tolist())
+    for t in range(0, c.N, 256 * 29):
+        pos |= {t - 1, t, t + 255}
+    pos |= set(range(c.N - 8, c.N))
+    pos = np.array(sorted(q for q in pos if 0 <= q < c.N), dtype=np.int64)
+    ref = c.oracle_engram(pos)
+    sel = torch.from_numpy(pos).to(c.dev)
+    got = np.stack([out[m * c.N + sel].double().cpu().numpy() for m in range(c.M)])
+    err = rel_err(got, ref["out"])
+    print(f"[tile walk] {name} rel err {err:.3e} over {len(pos)} positions")
+    assert err < TOL[wl["act_dtype"]]
+
+
 def test_causality_on_gpu():
     # Editing later tokens leaves earlier outputs bitwise unchanged, conv
     # included (Engram explainer, validation).
