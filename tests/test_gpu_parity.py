@@ -314,6 +314,22 @@ def test_engram_fusion_tile_walk(name):
     err = rel_err(got, ref["out"])
     print(f"[tile walk] {name} rel err {err:.3e} over {len(pos)} positions")
     assert err < TOL[wl["act_dtype"]]
+    # Every tile of the walk ran: with the workspace and the output filled
+    # with NaN bytes beforehand, the stage calls leave no output NaN (a tile
+    # left out would leave its v or partial sums NaN, and with them every
+    # output that depends on them), and they equal pg_forward bit for bit.
+    e = c.run_index_gather()
+    f = c.fuse(0)
+    ws = torch.full((max(pg.pg_workspace_size(None, f, c.B, c.T), 256),), 0xFF,
+                    dtype=torch.uint8, device=c.dev)
+    out2 = c.out_buffer()
+    out2.view(torch.uint8).fill_(0xFF)
+    pg.pg_engram_project(f, e, c.B, c.T, c.W, c.resid, ws)
+    pg.pg_engram_gate(f, c.B, c.T, ws)
+    pg.pg_engram_mix(f, c.B, c.T, c.resid, out2, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out2.float()).all())
+    assert torch.equal(out2.view(torch.uint8), out.view(torch.uint8))
 
 
 def test_causality_on_gpu():
