@@ -41,7 +41,7 @@
 // staging's 16-byte chunks sit at chunk ^ (row & 31) so a half-wave's reads
 // of one column block hit distinct banks.
 //
-// With bf16 operands and a slot count that is a multiple of 4 the kernel is
+// With a slot count that is a multiple of 4 (bf16 or E4M3) the kernel is
 // persistent: one block per CU walks its XCD's tiles, and each tile's
 // epilogue turns the K walk to the next tile, whose gamma vectors and slots
 // 0-2 load into the LDS the epilogue frees as it goes (slot k's buffer held
@@ -130,7 +130,6 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* E,
   const int tid_k = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid_k >> 6), lane_k = tid_k & 63;
   const int wm = wave / WGN, wn = wave % WGN;
-  static_assert(!(F8 && P), "the persistent form is bf16 only");
   // Tiles are numbered so that each XCD (blocks are dealt round-robin to the
   // 8 XCDs) runs a contiguous range of them, walked in groups of 8 M tiles
   // N-major: concurrent tiles share their E and W panels in one L2. One
@@ -452,13 +451,21 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* E,
       };
 
       // prologue: periods -4 .. -1 (slots 0-3); slot 0 landed; its fragments read
+      if (fresh) {
 #pragma unroll
-      for (int p = -4; p < 0; ++p) {
-        issue_half(p, 0);
-        issue_half(p, 1);
+        for (int p = -4; p < 0; ++p) {
+          issue_half(p, 0);
+          issue_half(p, 1);
+        }
+        wait_slot(0, 0);
+        bar();
+      } else {
+        // as in the bf16 loop below
+        wait_vm<2 * LS>();
+        bar();
+        issue_half(-1, 0);
+        issue_half(-1, 1);
       }
-      wait_slot(0, 0);
-      bar();
       read_slot(0, fa[0], fb[0]);
       using steady_t = std::integral_constant<bool, true>;
       using generic_t = std::integral_constant<bool, false>;
@@ -859,12 +866,10 @@ hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const 
   ep.f8_sb = 127 - se;
   const int64_t Nout = (1 + Mbr) * d;
   const int64_t blocks = ((N + 255) / 256) * ((Nout + 255) / 256);
-  const int64_t KS = E / 32;
-  if (f8) {
-    hipLaunchKernelGGL((engram_slot_kernel<true, false>), dim3((unsigned)blocks), dim3(512), 0,
-                       s, static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
-                       (int)Nout, (int)E, ep);
-  } else if (KS % 4 == 0) {
+  const int64_t KS = E / (f8 ? 64 : 32);
+  const auto* ep8 = static_cast<const uint8_t*>(e);
+  const auto* W8 = static_cast<const uint8_t*>(W);
+  if (KS % 4 == 0) {
     // one block per CU (a multiple of 8 blocks, so every XCD has as many)
     int cus = 0;
     const hipError_t err = cu_count(&cus);
@@ -872,13 +877,18 @@ hipError_t launch_engram_pass1_slots(const void* e, int64_t N, int64_t E, const 
     int64_t grid = cus / 8 * 8;
     if (grid < 8) grid = 8;
     if (grid > (blocks + 7) / 8 * 8) grid = (blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL((engram_slot_kernel<false, true>), dim3((unsigned)grid), dim3(512), 0, s,
-                       static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
-                       (int)Nout, (int)E, ep);
+    if (f8)
+      hipLaunchKernelGGL((engram_slot_kernel<true, true>), dim3((unsigned)grid), dim3(512), 0, s,
+                         ep8, W8, N, (int)Nout, (int)E, ep);
+    else
+      hipLaunchKernelGGL((engram_slot_kernel<false, true>), dim3((unsigned)grid), dim3(512), 0,
+                         s, ep8, W8, N, (int)Nout, (int)E, ep);
+  } else if (f8) {
+    hipLaunchKernelGGL((engram_slot_kernel<true, false>), dim3((unsigned)blocks), dim3(512), 0,
+                       s, ep8, W8, N, (int)Nout, (int)E, ep);
   } else {
     hipLaunchKernelGGL((engram_slot_kernel<false, false>), dim3((unsigned)blocks), dim3(512), 0,
-                       s, static_cast<const uint8_t*>(e), static_cast<const uint8_t*>(W), N,
-                       (int)Nout, (int)E, ep);
+                       s, ep8, W8, N, (int)Nout, (int)E, ep);
   }
   return hipGetLastError();
 }
