@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -139,11 +140,20 @@ def algorithmic_costs(wl, fp8=False):
                 **extra)
 
 
+def code_text(text):
+    """A kernel source's code: // comments, trailing blanks and empty lines
+    dropped (the sources have no /* */ comments and no // inside strings), so
+    that counters taken on a kernel stay attached to it when only its
+    comments change."""
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -338,8 +338,9 @@ __global__ __launch_bounds__(512, 1) void engram_slot_kernel(const uint8_t* E,
         dma4(ep.gamma_k + c0 + wave * 64, (uint32_t)lane * 4, lds0 + kGamOff + BN * 4 + wave * 256);
       }
     };
-    // a P block's later tiles had their gamma vectors and first four slots
-    // requested during the previous tile's epilogue
+    // a P block's later tiles had their gamma vectors and slots 0-2 requested
+    // during the previous tile's epilogue (slot 3 goes out after the first
+    // barrier below)
     const bool fresh = !P || jt == 0;
     if constexpr (P) {
       // wave 0 works out tile jt + 1 while the block waits for slot 0
