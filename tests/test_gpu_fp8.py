@@ -20,7 +20,7 @@ import oracle
 from oracle import fp8
 from synth import configs
 from tests.gpu_inputs import Case, rel_err
-from tests.test_gpu_parity import RAGGED, small_wl
+from tests.test_gpu_parity import RAGGED, TILE_WALK, sample_positions, small_wl
 
 pytestmark = pytest.mark.gpu
 
@@ -213,6 +213,55 @@ def test_forward_fp8_vs_oracle_and_stages(name):
     err = rel_err(got, ref["out"])
     print(f"[fp8 forward] {name} rel err {err:.3e}")
     assert err < (TOL if wl["gate"] == "scalar" else TOL_ENGRAM)
+
+
+def test_forward_fp8_tile_walk():
+    # The E4M3 fused projection walks 1,600 tiles on one block per CU (20
+    # slots of 64 elements), several per block, the last M tile ragged: every
+    # output written (workspaces and outputs NaN-filled beforehand) and equal
+    # between pg_forward_fp8 and its two stages; sampled positions, tile edges
+    # and the ragged tile against the oracle on dequantised operands.
+    wl = small_wl(4, gamma="random", **TILE_WALK["E1280_d512_M3_N51000"])
+    print("[fp8 tile walk] E1280_d512_M3_N51000", flush=True)
+    c = Case(wl)
+    se = SE[wl["table_dtype"]]
+    W8, Wq = _w8(c)
+    W8t = _u8(W8, c.dev)
+    f = c.fuse()
+
+    def nan_bytes(n):
+        return torch.full((max(n, 256),), 0xFF, dtype=torch.uint8, device=c.dev)
+
+    ws = nan_bytes(pg.pg_workspace_size(c.layout, f, c.B, c.T))
+    out = c.out_buffer()
+    out.view(torch.uint8).fill_(0xFF)
+    pg.pg_forward_fp8(c.layout, c.table, f, c.tokens, c.cmap, W8t, se, SW, c.resid, out, ws)
+    e8 = torch.empty(c.N, c.E, dtype=torch.uint8, device=c.dev)
+    pg.pg_index_gather_fp8(c.layout, c.table, c.tokens, c.cmap, se, e8)
+    ws2 = nan_bytes(pg.pg_workspace_size(None, f, c.B, c.T))
+    out2 = c.out_buffer()
+    out2.view(torch.uint8).fill_(0xFF)
+    pg.pg_project_gate_fp8(f, e8, c.B, c.T, W8t, se, SW, c.resid, out2, ws2)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+    qt = _Fp8Table(c, se)
+    pos = set(sample_positions(c, n_random=48).tolist())
+    for t in range(0, c.N, 256 * 29):
+        pos |= {t - 1, t, t + 255}
+    pos |= set(range(c.N - 8, c.N))
+    pos = np.array(sorted(q for q in pos if 0 <= q < c.N), dtype=np.int64)
+    gh, gk, gu, cw = c.eng_np
+    N = c.N
+    ref = oracle.forward_engram(c.lay_d, c.pad, c.tokens_np, c.cmap_np, "bf16", qt.fetch, Wq,
+                                c.d, c.M, gh, gk, gu, cw, wl["conv_dil"], wl["eps"],
+                                lambda m, fl: c.resid_rows([m * N + fl])[0].astype(np.float64),
+                                positions=pos)
+    sel = torch.from_numpy(pos).to(c.dev)
+    got = np.stack([out[m * c.N + sel].double().cpu().numpy() for m in range(c.M)])
+    err = rel_err(got, ref["out"])
+    print(f"[fp8 tile walk] rel err {err:.3e} over {len(pos)} positions")
+    assert err < TOL_ENGRAM
 
 
 def test_fp8_entry_points_reject_bad_arguments():
