@@ -74,3 +74,20 @@ def test_probe_copies_set_the_scale_and_request_sizes_give_bytes(tmp_path):
     assert g["read_requests"]["bytes"] == 1600 * 128 + 10 * 64
     assert ent["copy_scale"]["copy_read_requests"]["bytes"] == (1 << 30) + 10 * 64
     assert g["source_digest"] == b.source_digest(b.KERNEL_SOURCES["gather"])
+
+
+def test_source_digest_follows_code_not_comments(tmp_path, monkeypatch):
+    # The digest that keeps counter figures attached to a kernel: an edit to
+    # comments or blank lines keeps it, any edit to the code changes it.
+    src = tmp_path / "k.hip"
+    base = "// header\nint f(int x) {\n  return x + 1;  // one\n}\n"
+    src.write_text(base)
+    b = _bench()
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    d0 = b.source_digest(["k.hip"])
+    src.write_text("// header, reworded\n\nint f(int x) {   \n  return x + 1;  // one more\n}\n")
+    assert b.source_digest(["k.hip"]) == d0
+    src.write_text(base.replace("x + 1", "x + 2"))
+    assert b.source_digest(["k.hip"]) != d0
+    src.write_text(base.replace("return", "return -"))
+    assert b.source_digest(["k.hip"]) != d0
